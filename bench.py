@@ -1,0 +1,166 @@
+#!/usr/bin/env python3
+"""Benchmark: one continuous-batching decode step on one MI355X.
+
+Workload (seeded, synthetic): 256 sequences with context lengths uniform in
+[64, 4096], 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
+scattered over a pool of total blocks + 10% drawn from a shuffled free list.
+A step = pa_reshape_and_cache (one new token per sequence, through
+slot_mapping) + pa_decode over context + 1 (the decode kernel and, for the
+sequences longer than one 512-token partition, the log-sum-exp merge).
+Inputs are resident in HBM before timing starts.
+
+Prints one JSON line:
+  value       effective KV GB/s of the whole step = B_kv / step time, with
+              B_kv = sum_s L_s * 2 * Hkv * d * 2 bytes (live K and V read
+              once; tail slots of partial blocks not counted)
+  roofline    pa_decode's achieved B_kv / (mean duration of its launches,
+              HIP events on its stream over the timed steps) against the
+              8 TB/s HBM peak
+  cpu_baseline  the float64 CPU oracle on the same step, host cores
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention effective KV GB/s (% of HBM peak) + decode seqs/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time the oracle baseline accumulates")
+    ap.add_argument("--partition-size", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(b, seconds):
+    import oracle
+    from paged_kv_cache_400_amd.workload import bits
+    kp, vp = bits(b.k_cache).copy(), bits(b.v_cache).copy()
+    nk, nv, q = bits(b.new_key), bits(b.new_value), bits(b.q)
+    reps, total = 0, 0.0
+    while reps == 0 or total < seconds:
+        t0 = time.perf_counter()
+        oracle.reshape_and_cache(nk, nv, kp, vp, b.slot_mapping)
+        oracle.decode(q, kp, vp, b.block_tables, b.seq_lens, b.scale, oracle.BF16)
+        total += time.perf_counter() - t0
+        reps += 1
+    t = total / reps
+    return {
+        "value": round(b.kv_bytes() / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"the whole step ({len(b.slot_mapping)}-token append + decode of all "
+                   f"{b.num_seqs * b.num_q_heads} rows), float64, {reps} repetition(s) of "
+                   f"{t:.2f} s"),
+        "seqs_per_s": round(b.num_seqs / t, 2),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_400_amd as pa
+    from paged_kv_cache_400_amd import workload as wl
+
+    b = wl.make_mixed_step()
+    dev = wl.to_device(b, "cuda:0")
+    S, Hq, d = b.q.shape
+    MB, bs = b.max_blocks_per_seq, b.block_size
+    ws_bytes = pa.decode_workspace_bytes(S, Hq, d, MB, bs, args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(dev["q"])
+
+    def append():
+        pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"], dev["v_cache"],
+                             dev["slot_mapping"])
+
+    def decode():
+        pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
+                  scale=b.scale, partition_size=args.partition_size, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        append()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        append()
+        ev[i][0].record()
+        decode()
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    ms_decode = sum(a.elapsed_time(z) for a, z in ev) / K
+
+    kv = b.kv_bytes()
+    gbs_step = kv / (ms_step * 1e-3) / 1e9
+    gbs_decode = kv / (ms_decode * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs_step, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mixed_step: 256 seqs, context uniform[64,4096] + 1 appended token, "
+                        "32 q / 8 kv heads, d 128, bf16 (f32 accumulate), block 16, "
+                        "shuffled pool of blocks+10%",
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": b.num_kv_heads, "head_dim": d,
+            "block_size": bs, "num_blocks": b.num_blocks, "max_blocks_per_seq": MB,
+            "partition_size": args.partition_size or 512, "kv_bytes": kv,
+            "tokens": int(b.seq_lens.sum()),
+        },
+        "frac_of_hbm_peak": round(gbs_step / HBM_PEAK_GBS, 4),
+        "decode_seqs_per_s": round(S / (ms_step * 1e-3), 1),
+        "decode_ms": round(ms_decode, 5),
+        "decode_only_gbs": round(gbs_decode, 2),
+        "roofline": {
+            "kernel": "pa_decode (pa_decode_valu + pa_splitk_reduce)",
+            "bound": "hbm",
+            "achieved": round(gbs_decode, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs_decode / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if args.cpu_baseline == "on":
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * pa.h -- C ABI of libpa: decode attention over a paged KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations are the ones the PagedAttention pages describe:
+ *   - "What problem does PagedAttention solve, and what is continuous
+ *     batching?" (datarekha), section "How PagedAttention works": KV stored
+ *     in fixed-size blocks of a shared pool; a per-request block table maps
+ *     logical block number to physical block; the attention kernel follows
+ *     the table when it reads keys and values; blocks may be shared and a
+ *     diverging candidate gets a private copy (copy-on-write);
+ *   - same page, "Why the KV cache becomes the problem": each decode step
+ *     reads the stored keys/values and appends a little new data;
+ *   - "Continuous Batching & Paged Attention" (topicspectrum), sections
+ *     "Attention needs memory that grows with the conversation" (attention
+ *     of the current position against the cached keys/values) and "Paged
+ *     attention borrows a trick from operating systems" (a growing request
+ *     attaches another block).
+ *
+ * Layouts (all row-major, contiguous, on one GPU, 16-byte aligned):
+ *   q, out          [num_seqs][num_q_heads][head_dim]
+ *   k_cache/v_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens        int32 [num_seqs]
+ *   key/value       [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping    int32 [num_tokens]
+ *   block_mapping   int32 [num_pairs][2]  (src, dst)
+ * Position t of sequence s lives in physical block block_tables[s][t / bs]
+ * at offset t % bs; its flat slot is block * bs + t % bs.  Query head h
+ * reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions:
+ *   - Ownership: the caller owns every buffer.  The library allocates
+ *     nothing and keeps no per-call state; scratch comes from `workspace`.
+ *   - Execution: every call only enqueues work on `stream` and returns; it
+ *     never synchronises.  All array pointers are device pointers.
+ *   - Errors: a non-PA_OK status means nothing was enqueued (except
+ *     PA_ERR_HIP, a failed launch).  pa_last_error() gives the calling
+ *     thread's message for its last failed call.
+ *   - Only host-visible arguments are validated.  Device-side contents that
+ *     break the contract (a block id outside [0, num_blocks), a sequence
+ *     longer than its table, a slot outside the pool) are never
+ *     dereferenced: decode writes NaN rows for that sequence, the append
+ *     and the copy skip that entry.
+ *   - Zero-sized work (num_seqs, num_tokens or num_pairs == 0) is a no-op.
+ *   - Thread safety: no global mutable state beyond the thread-local error
+ *     text.  Calls that touch the same buffers on different streams race.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = 2,        /* inconsistent sizes, or a misaligned pointer      */
+  PA_ERR_UNSUPPORTED = 3,  /* dtype, head_dim, block_size or group not built   */
+  PA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required       */
+  PA_ERR_HIP = 5           /* the HIP runtime refused a launch                 */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F16 = 0,   /* IEEE binary16 */
+  PA_BF16 = 1   /* bfloat16      */
+} pa_dtype;
+
+/*
+ * Decode attention of one query token per sequence over its paged cache.
+ *
+ *   out[s][h][:] = sum_{t < L_s} softmax_t(scale * q[s][h] . K_t) V_t
+ *
+ * with K_t, V_t read through block_tables[s] from KV head
+ * h / (num_q_heads / num_kv_heads), L_s = seq_lens[s].  L_s = 0 gives a
+ * zero row.  Slots at positions >= L_s and table entries past
+ * ceil(L_s / block_size) are never read (they may hold anything, NaN
+ * included).  Scores, softmax and sums are float32; out is rounded to
+ * `dtype` (round to nearest even).
+ *
+ * Supported: dtype F16/BF16 (q, pools and out share it); head_dim 64 or
+ * 128; block_size 8, 16 or 32; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ *
+ * Long sequences are split into partitions of `partition_size` positions
+ * (0 = automatic; otherwise a positive multiple of block_size with at most
+ * 512 blocks per partition).  Each partition's softmax state is written to
+ * `workspace` and merged by log-sum-exp in a second kernel.  The workspace
+ * needs pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents
+ * on entry do not matter and on return are unspecified.
+ *
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, num_q_heads not a
+ * multiple of num_kv_heads, bad partition_size, misaligned pointer),
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes pa_decode needs for these sizes: an upper bound computed
+ * from max_blocks_per_seq * block_size (no device memory is read).  0 when no
+ * sequence can need more than one partition, or when an argument is invalid
+ * (pa_decode then reports the error).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_size);
+
+/*
+ * Append: for each token i with slot_mapping[i] >= 0 and each KV head h,
+ * k_cache[slot / bs][h][slot % bs][:] = key[i][h][:] (and the same for
+ * value), as bit copies.  A negative slot skips the token (padding).
+ * Non-negative slots must be distinct (duplicates race); slots >= num_blocks
+ * * block_size are skipped.
+ *
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (dtype, head_dim not
+ * a multiple of 8 in [8, 1024], block_size not in {8, 16, 32}), PA_ERR_HIP.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                               void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Copy-on-write data movement: for each pair (src, dst) of block_mapping,
+ * block dst of both pools (all KV heads and slots) becomes a bit copy of
+ * block src.  A src may appear in several pairs; dsts must be distinct and
+ * no dst may be a src (then the result equals a copy from a snapshot taken
+ * before the call).  Pairs with an id outside [0, num_blocks) are skipped.
+ *
+ * Errors: as pa_reshape_and_cache.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream);
+
+/* Static name of a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pa_last_error(void);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,17 @@
+"""Paged-KV-cache decode attention for AMD MI355X (gfx950).
+
+The compute lives in ``libpa.so`` (hand-written HIP kernels behind the C ABI
+of ``include/pa.h``); :mod:`.binding` is its Python binding.  Importing this
+package does not load the library; the first use of ``decode``,
+``reshape_and_cache``, ``copy_blocks`` or ``decode_workspace_bytes`` does,
+and fails loudly if it has not been built.
+"""
+_BINDING_NAMES = ("decode", "reshape_and_cache", "copy_blocks", "decode_workspace_bytes",
+                  "PaError", "abi_version", "LIB_PATH")
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,175 @@
+"""Python binding of libpa (include/pa.h): argument marshalling only.
+
+Every function checks the tensors' device, dtype, shape and contiguity,
+passes their device pointers and the current HIP stream of their device to
+the C ABI, and raises :class:`PaError` with the library's message on a
+non-OK status.  No step of the computation runs here; PyTorch supplies the
+memory and the stream.  If ``libpa.so`` has not been built the import fails
+loudly: there is no fallback.
+"""
+import ctypes
+import os
+
+import torch  # first: libpa binds to the HIP runtime torch has loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
+PA_F16, PA_BF16 = 0, 1
+_DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+# (name, restype, argtypes) for every entry point of include/pa.h
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, ctypes.c_int, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      ctypes.c_int, _vp]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_abi_version": (ctypes.c_int32, []),
+}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_lib.pa_status_string(status).decode()}: {message}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with paged_kv_cache_400_amd/build.py "
+            "(hipcc, gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return int(_lib.pa_abi_version())
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PaError(status, _lib.pa_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dims=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size,
+                           partition_size=0) -> int:
+    return int(_lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                              max_blocks_per_seq, block_size, partition_size))
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_size=0, out=None,
+           workspace=None):
+    """out[s][h] = softmax(scale * q[s][h] . K) V over the sequence's paged K/V.
+
+    q [S][Hq][d]; k_cache/v_cache [NB][Hkv][bs][d]; block_tables int32
+    [S][MB]; seq_lens int32 [S].  ``workspace`` (a uint8 tensor) is allocated
+    when needed and not given.
+    """
+    _need(q, "q", 3)
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    _need(k_cache, "k_cache", 4, q.dtype, dev)
+    _need(v_cache, "v_cache", 4, q.dtype, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("inconsistent shapes between q, the pools, block_tables and seq_lens")
+    MB = block_tables.shape[1]
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", 3, q.dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_bytes(S, Hq, d, MB, bs, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None, None, dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                          _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB,
+                          float(scale), int(partition_size), _DT[q.dtype], _ptr(workspace),
+                          ws_bytes, _stream(dev)))
+    return out
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
+    """k_cache/v_cache[slot // bs][:, slot % bs] = key/value[i] for slot >= 0."""
+    _need(key, "key", 3)
+    dev = key.device
+    if key.dtype not in _DT:
+        raise ValueError(f"key must be float16 or bfloat16, got {key.dtype}")
+    _need(value, "value", 3, key.dtype, dev)
+    _need(k_cache, "k_cache", 4, key.dtype, dev)
+    _need(v_cache, "v_cache", 4, key.dtype, dev)
+    _need(slot_mapping, "slot_mapping", 1, torch.int32, dev)
+    T, Hkv, d = key.shape
+    NB, Hkv2, bs, d2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or Hkv2 != Hkv or d2 != d or \
+            slot_mapping.shape[0] != T:
+        raise ValueError("inconsistent shapes between key/value, the pools and slot_mapping")
+    _check(_lib.pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(slot_mapping), T, Hkv, d, bs, NB, _DT[key.dtype],
+                                     _stream(dev)))
+
+
+def copy_blocks(k_cache, v_cache, block_mapping):
+    """For each (src, dst) row of block_mapping: block dst := block src (K and V)."""
+    _need(k_cache, "k_cache", 4)
+    dev = k_cache.device
+    if k_cache.dtype not in _DT:
+        raise ValueError(f"k_cache must be float16 or bfloat16, got {k_cache.dtype}")
+    _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
+    _need(block_mapping, "block_mapping", 2, torch.int32, dev)
+    if v_cache.shape != k_cache.shape or block_mapping.shape[1] != 2:
+        raise ValueError("pools must match and block_mapping must be [n][2]")
+    NB, Hkv, bs, d = k_cache.shape
+    _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                               block_mapping.shape[0], Hkv, d, bs, NB, _DT[k_cache.dtype],
+                               _stream(dev)))

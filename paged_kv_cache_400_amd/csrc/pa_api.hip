@@ -1,0 +1,221 @@
+// pa_api.hip -- the C ABI declared in include/pa.h: argument validation,
+// partition and workspace sizing, dispatch to the kernel launchers, and the
+// thread-local error text.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int32_t kAutoPartition = 512;
+constexpr int64_t kMaxThreadsPerLaunch = (int64_t)1 << 32;
+
+// Partition size actually used; 0 if partition_size is invalid.
+int32_t resolve_partition(int32_t partition_size, int32_t block_size) {
+  const int32_t p = partition_size == 0 ? kAutoPartition : partition_size;
+  if (p <= 0 || block_size <= 0 || p % block_size != 0) return 0;
+  if (p / block_size > pa::decode_max_partition_blocks()) return 0;
+  return p;
+}
+
+int64_t partitions_needed(int32_t max_blocks_per_seq, int32_t block_size, int32_t part) {
+  const int64_t max_len = (int64_t)max_blocks_per_seq * block_size;
+  return (max_len + part - 1) / part;
+}
+
+bool supported_cache_dims(int32_t head_dim, int32_t block_size) {
+  return head_dim >= 8 && head_dim <= 1024 && head_dim % 8 == 0 &&
+         (block_size == 8 || block_size == 16 || block_size == 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0)
+    return 0;
+  const int32_t part = resolve_partition(partition_size, block_size);
+  if (part == 0) return 0;
+  const int64_t pmax = partitions_needed(max_blocks_per_seq, block_size, part);
+  if (pmax <= 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * pmax;
+  return (size_t)(rows * head_dim * (int64_t)sizeof(float) + rows * 2 * (int64_t)sizeof(float));
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_decode: sizes must be positive (num_seqs >= 0): S=%d Hq=%d Hkv=%d d=%d "
+                "bs=%d MB=%d NB=%d",
+                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                num_blocks);
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d is not PA_F16 or PA_BF16", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not in {64, 128}", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not in {8, 16, 32}", block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "pa_decode: num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: query group %d not in {1, 2, 4, 8}", group);
+  const int32_t part = resolve_partition(partition_size, block_size);
+  if (part == 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_decode: partition_size %d must be 0 or a positive multiple of block_size "
+                "%d with at most %d blocks",
+                partition_size, block_size, pa::decode_max_partition_blocks());
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "pa_decode: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE, "pa_decode: out, q, k_cache and v_cache must be 16-byte aligned");
+  const int64_t pmax = partitions_needed(max_blocks_per_seq, block_size, part);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * pmax;
+  if (units * 256 >= kMaxThreadsPerLaunch || pmax > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_decode: %lld work units exceed one launch",
+                (long long)units);
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                max_blocks_per_seq, block_size, partition_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (need > 0 && !aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "pa_decode: workspace must be 16-byte aligned");
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * pmax;
+  a.ws_acc = need ? (float*)workspace : nullptr;
+  a.ws_ml = need ? (float2*)((char*)workspace + rows * head_dim * sizeof(float)) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.part = part;
+  a.pmax = (int32_t)pmax;
+  a.qk_scale = scale * 1.4426950408889634f;
+  a.bf16 = dtype == PA_BF16;
+  a.stream = stream;
+  const hipError_t e = pa::launch_decode(a);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                               void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_reshape_and_cache: sizes must be positive (num_tokens >= 0): T=%d Hkv=%d "
+                "d=%d bs=%d NB=%d",
+                num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: dtype %d not supported", (int)dtype);
+  if (!supported_cache_dims(head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_reshape_and_cache: head_dim %d (multiple of 8 in [8, 1024]) or block_size "
+                "%d (8, 16, 32) not supported",
+                head_dim, block_size);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "pa_reshape_and_cache: a required pointer is NULL");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE, "pa_reshape_and_cache: key, value and pools must be 16-byte aligned");
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+  if (total + 255 >= kMaxThreadsPerLaunch)
+    return fail(PA_ERR_SHAPE, "pa_reshape_and_cache: too many tokens for one launch");
+  const hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+                                                    num_tokens, num_kv_heads, head_dim,
+                                                    block_size, num_blocks, stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_reshape_and_cache: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_copy_blocks: sizes must be positive (num_pairs >= 0): n=%d Hkv=%d d=%d "
+                "bs=%d NB=%d",
+                num_pairs, num_kv_heads, head_dim, block_size, num_blocks);
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: dtype %d not supported", (int)dtype);
+  if (!supported_cache_dims(head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_copy_blocks: head_dim %d (multiple of 8 in [8, 1024]) or block_size %d "
+                "(8, 16, 32) not supported",
+                head_dim, block_size);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping)
+    return fail(PA_ERR_NULL, "pa_copy_blocks: a required pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: pools must be 16-byte aligned");
+  const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
+                                              num_kv_heads, head_dim, block_size, num_blocks,
+                                              stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// pa_device.h -- device helpers shared by the libpa kernels (gfx950).
+//
+// Element formats: IEEE binary16 and bfloat16, stored as raw 16-bit words;
+// two neighbouring elements share one 32-bit register word (element 2k in
+// the low half, 2k+1 in the high half).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct F16 {};
+struct BF16 {};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- widening of packed pairs -------------------------------------------
+template <typename T> __device__ __forceinline__ float lo_f32(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi_f32(uint32_t w);
+
+template <> __device__ __forceinline__ float lo_f32<BF16>(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+template <> __device__ __forceinline__ float hi_f32<BF16>(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+template <> __device__ __forceinline__ float lo_f32<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <> __device__ __forceinline__ float hi_f32<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// ---- a.lo*b.lo + a.hi*b.hi + c, float32 accumulate (v_dot2_f32_*) -------
+template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+
+template <> __device__ __forceinline__ float dot2<F16>(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+template <> __device__ __forceinline__ float dot2<BF16>(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                         __builtin_bit_cast(bf162_t, b), c, false);
+}
+
+// ---- float -> 16-bit word, round to nearest even -----------------------
+template <typename T> __device__ __forceinline__ uint16_t to_bits(float x);
+
+template <> __device__ __forceinline__ uint16_t to_bits<F16>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);  // v_cvt_f16_f32, RNE
+}
+template <> __device__ __forceinline__ uint16_t to_bits<BF16>(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- 2^x on the transcendental unit (v_exp_f32; 2^-inf = 0) -------------
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- DPP lane exchange within 16-lane rows -----------------------------
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over groups of N consecutive lanes (N = 8 or 16); every lane of a
+// group ends with the same bits (each exchange adds a pair in both lanes).
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  if constexpr (N == 16) x += dpp<kRowMirror>(x);
+  return x;
+}
+
+}  // namespace pa

@@ -1,0 +1,38 @@
+// pa_launch.h -- internal interface between the C ABI (pa_api.hip) and the
+// kernel launchers.  Arguments are already validated when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_acc;      // [S][Hq][pmax][D]   (pmax > 1 only)
+  float2* ws_ml;      // [S][Hq][pmax]      (m, l), m in base-2 units
+  int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq, num_blocks, part, pmax;
+  float qk_scale;     // scale * log2(e)
+  bool bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+int decode_max_partition_blocks();
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int32_t* slot_mapping,
+                                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                              int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, hipStream_t stream);
+
+}  // namespace pa

@@ -166,7 +166,7 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
                       head_dim: int, block_size: int, dtype: str, seed: int,
                       append: int = 1, num_blocks: Optional[int] = None,
                       pool_slack: float = 0.10, scale: Optional[float] = None,
-                      pad_tokens: int = 0) -> PagedBatch:
+                      pad_tokens: int = 0, placement_seed: Optional[int] = None) -> PagedBatch:
     """A batch of independent sequences (no sharing).
 
     ``context_lens[s]`` tokens are already in the pool; ``append`` (0 or 1)
@@ -174,6 +174,7 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     context + append.  Blocks for the context are taken from the free list in
     sequence order, then blocks attached by the append.  ``pad_tokens`` extra
     new-token rows with slot -1 are interleaved (the append skips them).
+    ``placement_seed`` (default ``seed``) changes only where blocks go.
     """
     ctx = np.asarray(context_lens, dtype=np.int32)
     S = len(ctx)
@@ -182,7 +183,7 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     need = sum(_blocks(int(L), bs) for L in lens)
     if num_blocks is None:
         num_blocks = int(math.ceil((1.0 + pool_slack) * need)) + 1
-    rng_place = np.random.default_rng([seed, 1, bs])
+    rng_place = np.random.default_rng([seed if placement_seed is None else placement_seed, 1, bs])
     free = _FreeList(num_blocks, rng_place)
     MB = max(1, max(_blocks(int(L), bs) for L in lens)) if S else 1
     tables = np.zeros((S, MB), dtype=np.int32)

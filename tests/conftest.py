@@ -24,3 +24,13 @@ def oracle_mod():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Name each GPU test on stderr before it runs, so a run that dies on the
+    device still says which case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write(f"\n[gpu-test] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield
