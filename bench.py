@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time the oracle baseline accumulates")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
+                    help="pa_decode (matrix-core kernel) or pa_decode_valu")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (a transfer of "
+                         "known size to scale HBM byte counters by)")
     return ap.parse_args()
 
 
@@ -95,7 +100,8 @@ def main():
 
     def decode():
         pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
-                  scale=b.scale, partition_size=args.partition_size, out=out, workspace=ws)
+                  scale=b.scale, partition_size=args.partition_size, out=out, workspace=ws,
+                  impl=args.impl)
 
     for _ in range(args.warmup):
         append()
@@ -148,7 +154,8 @@ def main():
         "decode_ms": round(ms_decode, 5),
         "decode_only_gbs": round(gbs_decode, 2),
         "roofline": {
-            "kernel": "pa_decode (pa_decode_valu + pa_splitk_reduce)",
+            "kernel": ("pa_decode (pa_decode_mfma + pa_splitk_reduce)" if args.impl == "mfma"
+                       else "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)"),
             "bound": "hbm",
             "achieved": round(gbs_decode, 2),
             "peak": HBM_PEAK_GBS,
@@ -157,6 +164,21 @@ def main():
             "traffic": None,
         },
     }
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        res["calibration_copy"] = {"bytes_read": n, "bytes_written": n,
+                                   "ms": round(c0.elapsed_time(c1), 5),
+                                   "gbs_read_plus_write": round(2 * n / (c0.elapsed_time(c1)
+                                                                         * 1e-3) / 1e9, 1)}
+        del src, dst
     if args.cpu_baseline == "on":
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(res), flush=True)

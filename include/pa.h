@@ -83,15 +83,16 @@ typedef enum pa_dtype {
  * h / (num_q_heads / num_kv_heads), L_s = seq_lens[s].  L_s = 0 gives a
  * zero row.  Slots at positions >= L_s and table entries past
  * ceil(L_s / block_size) are never read (they may hold anything, NaN
- * included).  Scores, softmax and sums are float32; out is rounded to
- * `dtype` (round to nearest even).
+ * included).  Scores, softmax and sums are float32; the softmax weights are
+ * rounded to `dtype` for the P.V product (the denominator sums the rounded
+ * weights); out is rounded to `dtype` (round to nearest even).
  *
  * Supported: dtype F16/BF16 (q, pools and out share it); head_dim 64 or
  * 128; block_size 8, 16 or 32; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  *
  * Long sequences are split into partitions of `partition_size` positions
- * (0 = automatic; otherwise a positive multiple of block_size with at most
- * 512 blocks per partition).  Each partition's softmax state is written to
+ * (0 = automatic; otherwise a positive multiple of 16 and of block_size,
+ * with at most 512 blocks per partition).  Each partition's softmax state is written to
  * `workspace` and merged by log-sum-exp in a second kernel.  The workspace
  * needs pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents
  * on entry do not matter and on return are unspecified.
@@ -106,6 +107,20 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                     float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode computed by the wave-level vector kernel instead of the
+ * matrix-core one: q.K as packed dot products reduced across the lanes of a
+ * row, P.V as float32 FMAs.  Same arguments, contract, workspace and errors
+ * as pa_decode; results agree to rounding (the two sum in different orders,
+ * and this kernel keeps P in float32).
+ */
+pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Workspace bytes pa_decode needs for these sizes: an upper bound computed

@@ -24,6 +24,8 @@ _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c
 SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_decode_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, ctypes.c_int, _vp]),
@@ -96,13 +98,16 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, 
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_size=0, out=None,
-           workspace=None):
+           workspace=None, impl="mfma"):
     """out[s][h] = softmax(scale * q[s][h] . K) V over the sequence's paged K/V.
 
     q [S][Hq][d]; k_cache/v_cache [NB][Hkv][bs][d]; block_tables int32
     [S][MB]; seq_lens int32 [S].  ``workspace`` (a uint8 tensor) is allocated
-    when needed and not given.
+    when needed and not given.  ``impl``: "mfma" (pa_decode) or "valu"
+    (pa_decode_valu).
     """
+    if impl not in ("mfma", "valu"):
+        raise ValueError(f"impl must be 'mfma' or 'valu', got {impl!r}")
     _need(q, "q", 3)
     dev = q.device
     if q.dtype not in _DT:
@@ -132,10 +137,10 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_si
     if workspace is not None:
         _need(workspace, "workspace", None, None, dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                          _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB,
-                          float(scale), int(partition_size), _DT[q.dtype], _ptr(workspace),
-                          ws_bytes, _stream(dev)))
+    fn = _lib.pa_decode if impl == "mfma" else _lib.pa_decode_valu
+    _check(fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+              _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB, float(scale),
+              int(partition_size), _DT[q.dtype], _ptr(workspace), ws_bytes, _stream(dev)))
     return out
 
 

@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescales them with VALU
+    # ops, which cannot read the accumulation registers directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -255,13 +255,16 @@ pa_decode_valu(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
   }
 }
 
-// Merge of the partitions of every (sequence, query head) with more than one.
+// Merge of the partitions of every (sequence, query head) with more than one:
+// one thread per output element; the partition states are read in batches of
+// 8 independent loads so the loop is not a chain of dependent load latencies.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 pa_splitk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
                  const float2* __restrict__ ws_ml, const int32_t* __restrict__ seq_lens,
                  int32_t hq, int32_t max_len, int32_t part, int32_t pmax) {
   constexpr int HPB = 256 / D;  // query heads per workgroup
+  constexpr int U = 8;
   const int s = blockIdx.y;
   const int h = blockIdx.x * HPB + threadIdx.x / D;
   const int d = threadIdx.x % D;
@@ -274,15 +277,47 @@ pa_splitk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
   const float2* ml = ws_ml + r * pmax;
   const float* ac = ws_acc + r * pmax * D + d;
   float M = kNegInf;
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, ml[k].x);
+  for (int k0 = 0; k0 < nparts; k0 += U) {
+    float mk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mk[u] = (k0 + u < nparts) ? ml[k0 + u].x : kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mk[u]);
+  }
   float num = 0.0f, den = 0.0f;
-  for (int k = 0; k < nparts; ++k) {
-    const float2 v = ml[k];
-    const float f = exp2_fast(v.x - M);
-    num = fmaf(f, ac[(int64_t)k * D], num);
-    den = fmaf(f, v.y, den);
+  for (int k0 = 0; k0 < nparts; k0 += U) {
+    float2 v[U];
+    float a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = k0 + u < nparts;
+      v[u] = ok ? ml[k0 + u] : make_float2(kNegInf, 0.0f);
+      a[u] = ok ? ac[(int64_t)(k0 + u) * D] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = exp2_fast(v[u].x - M);
+      num = fmaf(f, a[u], num);
+      den = fmaf(f, v[u].y, den);
+    }
   }
   out[r * D + d] = to_bits<T>(num / den);
+}
+
+template <typename T, int D>
+static hipError_t launch_reduce_t(const DecodeArgs& a) {
+  constexpr int HPB = 256 / D;
+  const int hq = a.num_kv_heads * a.group;
+  hipLaunchKernelGGL((pa_splitk_reduce<T, D>),
+                     dim3((uint32_t)((hq + HPB - 1) / HPB), (uint32_t)a.num_seqs), dim3(256), 0,
+                     a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.seq_lens, hq,
+                     a.max_blocks_per_seq * a.block_size, a.part, a.pmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const DecodeArgs& a) {
+  if (a.bf16) return a.head_dim == 64 ? launch_reduce_t<BF16, 64>(a) : launch_reduce_t<BF16, 128>(a);
+  return a.head_dim == 64 ? launch_reduce_t<F16, 64>(a) : launch_reduce_t<F16, 128>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,13 +331,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
                      a.pmax, a.qk_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.pmax <= 1) return e;
-  constexpr int HPB = 256 / D;
-  const int hq = a.num_kv_heads * G;
-  hipLaunchKernelGGL((pa_splitk_reduce<T, D>), dim3((uint32_t)((hq + HPB - 1) / HPB),
-                                                    (uint32_t)a.num_seqs),
-                     dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.seq_lens,
-                     hq, a.max_blocks_per_seq * BS, a.part, a.pmax);
-  return hipGetLastError();
+  return launch_splitk_reduce(a);
 }
 
 template <typename T, int D, int BS>

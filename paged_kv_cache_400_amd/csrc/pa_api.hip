@@ -24,10 +24,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int32_t kAutoPartition = 512;
 constexpr int64_t kMaxThreadsPerLaunch = (int64_t)1 << 32;
 
-// Partition size actually used; 0 if partition_size is invalid.
+// Partition size actually used; 0 if partition_size is invalid.  Partitions
+// start at multiples of 16 positions (the decode kernels' tile) and of the
+// block size.
 int32_t resolve_partition(int32_t partition_size, int32_t block_size) {
   const int32_t p = partition_size == 0 ? kAutoPartition : partition_size;
-  if (p <= 0 || block_size <= 0 || p % block_size != 0) return 0;
+  if (p <= 0 || block_size <= 0 || p % block_size != 0 || p % 16 != 0) return 0;
   if (p / block_size > pa::decode_max_partition_blocks()) return 0;
   return p;
 }
@@ -75,12 +77,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return (size_t)(rows * head_dim * (int64_t)sizeof(float) + rows * 2 * (int64_t)sizeof(float));
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
-                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+enum class Impl { kMfma, kValu };
+
+pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, float scale, int32_t partition_size, pa_dtype dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
@@ -104,8 +112,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int32_t part = resolve_partition(partition_size, block_size);
   if (part == 0)
     return fail(PA_ERR_SHAPE,
-                "pa_decode: partition_size %d must be 0 or a positive multiple of block_size "
-                "%d with at most %d blocks",
+                "pa_decode: partition_size %d must be 0 or a positive multiple of 16 and of "
+                "block_size %d, with at most %d blocks",
                 partition_size, block_size, pa::decode_max_partition_blocks());
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
@@ -147,10 +155,38 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.qk_scale = scale * 1.4426950408889634f;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = pa::launch_decode(a);
+  const hipError_t e = impl == Impl::kMfma ? pa::launch_decode_mfma(a) : pa::launch_decode(a);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, scale, partition_size, dtype, workspace, workspace_bytes,
+                     stream);
+}
+
+pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(Impl::kValu, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, scale, partition_size, dtype, workspace, workspace_bytes,
+                     stream);
 }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,

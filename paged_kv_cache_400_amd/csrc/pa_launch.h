@@ -23,7 +23,11 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+// pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
+// (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a);
+hipError_t launch_splitk_reduce(const DecodeArgs& a);
 int decode_max_partition_blocks();
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,

@@ -18,7 +18,7 @@ MEAN_ABS = 1e-3
 ODT = {"f16": oracle.F16, "bf16": oracle.BF16}
 
 
-def gpu_step(b, partition_size=0, device="cuda:0", dev=None):
+def gpu_step(b, partition_size=0, device="cuda:0", dev=None, impl="mfma"):
     """copy_blocks -> reshape_and_cache -> decode on the GPU; returns (out, dev)."""
     dev = to_device(b, device) if dev is None else dev
     if len(b.block_mapping):
@@ -27,7 +27,7 @@ def gpu_step(b, partition_size=0, device="cuda:0", dev=None):
         pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"], dev["v_cache"],
                              dev["slot_mapping"])
     out = pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                    dev["seq_lens"], scale=b.scale, partition_size=partition_size)
+                    dev["seq_lens"], scale=b.scale, partition_size=partition_size, impl=impl)
     torch.cuda.synchronize()
     return out, dev
 

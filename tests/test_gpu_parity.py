@@ -51,12 +51,13 @@ def test_worked_example():
     compare(out, oracle_out(b, kp, vp), label="worked_example")
 
 
-def test_mixed_step_full_size():
+@pytest.mark.parametrize("impl", ["mfma", "valu"])
+def test_mixed_step_full_size(impl):
     b = wl.make_mixed_step()
-    out, dev = gpu_step(b)
+    out, dev = gpu_step(b, impl=impl)
     kp, vp = _check_pools(dev, b)
     pairs = sample_pairs(b, 24)
-    compare(out, oracle_out(b, kp, vp, pairs=pairs), pairs=pairs, label="mixed_step")
+    compare(out, oracle_out(b, kp, vp, pairs=pairs), pairs=pairs, label=f"mixed_step {impl}")
 
 
 def test_shared_prefix_copy_on_write():
@@ -76,10 +77,12 @@ def test_shared_prefix_copy_on_write():
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_long_context_split(bs):
     b = wl.make_long_context(bs)
-    out, dev = gpu_step(b)
+    dev = wl.to_device(b, "cuda:0")
     pairs = sample_pairs(b, 6, seed=bs)
-    kp, vp = wl.bits(b.k_cache), wl.bits(b.v_cache)
-    compare(out, oracle_out(b, kp, vp, pairs=pairs), pairs=pairs, label=f"long_context bs{bs}")
+    ref = oracle_out(b, wl.bits(b.k_cache), wl.bits(b.v_cache), pairs=pairs)
+    for impl in ("mfma", "valu"):
+        out, _ = gpu_step(b, dev=dev, impl=impl)
+        compare(out, ref, pairs=pairs, label=f"long_context bs{bs} {impl}")
 
 
 # ---------------------------------------------------------------- edge cases
@@ -87,20 +90,21 @@ def test_long_context_split(bs):
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
 
 
+@pytest.mark.parametrize("impl", ["mfma", "valu"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
-def test_ragged_edges(dtype, d, bs, g):
+def test_ragged_edges(dtype, d, bs, g, impl):
     """Lengths at and around tile, block and partition edges (partition 64 so
     most sequences split), empty sequences included, every group size."""
     hkv = 2
     b = wl.make_decode_batch("edges", EDGE_LENS, hkv * g, hkv, d, bs, dtype,
                              seed=100 + g + d + bs, append=1)
     for part in (64, 0):
-        out, dev = gpu_step(b, partition_size=part)
+        out, dev = gpu_step(b, partition_size=part, impl=impl)
         kp, vp = _check_pools(dev, b)
-        compare(out, oracle_out(b, kp, vp), label=f"edges part{part}")
+        compare(out, oracle_out(b, kp, vp), label=f"edges part{part} {impl}")
 
 
 def test_empty_and_single_token_sequences():
