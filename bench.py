@@ -21,6 +21,7 @@ Prints one JSON line:
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +31,34 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention effective KV GB/s (% of HBM peak) + decode seqs/s"
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per pa_decode call from the committed rocprofv3 FETCH_SIZE /
+# WRITE_SIZE summary; reported only while the kernel sources still hash to
+# the value recorded there (a changed kernel has no measured traffic).
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_mfma_mixed_step_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_400_amd", "csrc", f)
+                  for f in ("decode_mfma.hip", "decode.hip", "pa_device.h", "pa_launch.h")]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """(bytes per call, note) from the counter summary, or (None, reason)."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None, "no counter summary"
+    fields = dict(re.findall(r"^([a-z_0-9]+): (\S+)$", text, re.M))
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None, "kernel changed since the counters were taken"
+    return int(fields["traffic_bytes_per_call"]), os.path.relpath(TRAFFIC_SUMMARY, ROOT)
 
 
 def parse():
@@ -164,6 +193,11 @@ def main():
             "traffic": None,
         },
     }
+    traffic, note = measured_traffic()
+    if args.impl == "mfma" and traffic is not None:
+        res["roofline"]["traffic"] = traffic
+        res["roofline"]["traffic_over_algorithmic"] = round(traffic / kv, 4)
+    res["roofline"]["traffic_source"] = note if args.impl == "mfma" else "not profiled"
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
