@@ -8,8 +8,9 @@
 // that grows with the conversation").
 //
 // Work decomposition.  One workgroup (4 waves) per work unit
-// (sequence s, KV head kh, partition p); a partition is `part` consecutive
-// positions.  The G = Hq/Hkv query heads that share kh share every K/V load.
+// (sequence s, KV head kh, partition p), numbered partition-major so that
+// the XCDs share the work evenly (unit_of in pa_device.h); a partition is
+// `part` consecutive positions.  The G = Hq/Hkv query heads that share kh share every K/V load.
 // The unit stages its block ids in LDS, then its waves take 16-token (d 128)
 // or 32-token (d 64) tiles in turn:
 //   - lane layout: a token row is D/8 lanes, each holding 8 elements
@@ -58,11 +59,8 @@ pa_decode_valu(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
   __shared__ float s_l[kWaves][G];
   __shared__ int s_bad;
 
-  const int unit = blockIdx.x;
-  const int p = unit % pmax;
-  const int rest = unit / pmax;
-  const int kh = rest % hkv;
-  const int s = rest / hkv;
+  const Unit u = unit_of(blockIdx.x, hkv, pmax);
+  const int s = u.s, kh = u.kh, p = u.p;
   const int hq = hkv * G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

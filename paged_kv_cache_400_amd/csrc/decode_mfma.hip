@@ -2,7 +2,8 @@
 // cores (gfx950 MFMA), for head_dim 64/128, block 8/16/32, group 1..8.
 //
 // Same result and work decomposition as the VALU kernel (decode.hip): one
-// workgroup of 4 waves per (sequence, KV head, partition), waves taking
+// workgroup of 4 waves per (sequence, KV head, partition), numbered
+// partition-major so that the XCDs share the work evenly, waves taking
 // 16-position tiles in turn, a per-wave online softmax in base 2, a
 // log-sum-exp merge of the waves and, for split sequences, of the partitions.
 // How a wave handles a tile of 16 positions x G query heads:
@@ -123,11 +124,8 @@ pa_decode_mfma(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * GE::TILE];
   __shared__ int s_bad[kWaves];
 
-  const int unit = blockIdx.x;
-  const int p = unit % pmax;
-  const int rest = unit / pmax;
-  const int kh = rest % hkv;
-  const int s = rest / hkv;
+  const Unit u = unit_of(blockIdx.x, hkv, pmax);
+  const int s = u.s, kh = u.kh, p = u.p;
   const int hq = hkv * G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

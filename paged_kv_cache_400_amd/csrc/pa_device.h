@@ -84,4 +84,27 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+
+// ---- work-unit order ------------------------------------------------------
+// A decode launch has one workgroup per unit (sequence s, KV head kh,
+// partition p), num_seqs * hkv * pmax in all; units with p past a sequence's
+// last partition exit at once.  The hardware deals workgroup i to XCD i % 8,
+// and each XCD has its own L2 and dispatcher, so the order decides how the
+// work is split between XCDs.  Units are numbered partition-major:
+//   i = (pmax - 1 - p) * (num_seqs * hkv) + s * hkv + kh,
+// so consecutive workgroups walk the sequences and heads of one partition
+// index, each XCD gets every sequence in equal measure (with hkv = 8, XCD x
+// gets KV head x of every sequence), and the sparse high partition indices,
+// which only long sequences have, come first instead of leaving the chip
+// half idle at the end.  (Numbering (s, kh, p) with p fastest sent every
+// first partition to XCD 0 and every eighth to XCD 7.)
+struct Unit {
+  int s, kh, p;
+};
+__device__ __forceinline__ Unit unit_of(int i, int hkv, int pmax) {
+  const int per_part = (int)(gridDim.x / (unsigned)pmax);  // num_seqs * hkv
+  const int rest = i % per_part;
+  return Unit{rest / hkv, rest % hkv, pmax - 1 - i / per_part};
+}
+
 }  // namespace pa
