@@ -141,8 +141,8 @@ pa_decode_valu(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
       vr[i] = make_uint4(0u, 0u, 0u, 0u);
       if (valid[i]) {
         const int64_t off = (int64_t)s_bt[t / BS - blk0] * blk_stride + lane_off + (t % BS) * D;
-        kr[i] = *reinterpret_cast<const uint4*>(kc + off);
-        vr[i] = *reinterpret_cast<const uint4*>(vc + off);
+        kr[i] = load_stream(kc + off);
+        vr[i] = load_stream(vc + off);
       }
     }
 

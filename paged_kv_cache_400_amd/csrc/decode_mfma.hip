@@ -9,9 +9,9 @@
 // How a wave handles a tile of 16 positions x G query heads:
 //
 //  loads   K goes to registers, V goes straight from HBM into the wave's LDS
-//          tile (global_load_lds_dwordx4, no VGPRs).  Both are issued one
-//          tile ahead: the loop waits for tile k, issues tile k+1, then
-//          computes tile k.  Block ids are wave-uniform scalar loads; a
+//          tile (global_load_lds_dwordx4, no VGPRs), both with the
+//          streaming (nt) hint.  Both are issued one tile ahead: the loop
+//          waits for tile k, issues tile k+1, then computes tile k.  Block ids are wave-uniform scalar loads; a
 //          position past the end is clamped to the last valid one (so no
 //          unused slot is ever read) and its score is masked.
 //  q.K^T   S[t][h] = sum_d K[t][d] q[h][d] as D/32 v_mfma_f32_16x16x32
@@ -181,7 +181,7 @@ pa_decode_mfma(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
       const uint16_t* kr_base = (BS < kTile && t - t0 >= BS) ? kb1 : kb0;
       const uint16_t* ptr = kr_base + (t % BS) * D + grp * 8;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const uint4*>(ptr + c * 32);
+      for (int c = 0; c < KC; ++c) kr[c] = load_stream(ptr + c * 32);
     }
     // V: region i holds rows 4i..4i+3; lane l (< LANES) loads row 4i + l/(D/8),
     // chunk l%(D/8), landing at region i + 16*l bytes
@@ -194,7 +194,8 @@ pa_decode_mfma(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
       if (GE::LANES == 64 || lane < GE::LANES)
         __builtin_amdgcn_global_load_lds(
             (const void*)(vrow + (lane % (D / 8)) * 8),
-            (void __attribute__((address_space(3)))*)(vt + i * GE::REGION), 16, 0, 0);
+            (void __attribute__((address_space(3)))*)(vt + i * GE::REGION), 16, 0,
+            kCachePolicyStream);
     }
   };
 
