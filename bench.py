@@ -35,9 +35,15 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per pa_decode call from the committed rocprofv3 FETCH_SIZE /
 # WRITE_SIZE summary; reported only while the kernel sources still hash to
 # the value recorded there (a changed kernel has no measured traffic).
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_mfma_mixed_step_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_streamk_mixed_step_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_400_amd", "csrc", f)
-                  for f in ("decode_mfma.hip", "decode.hip", "pa_device.h", "pa_launch.h")]
+                  for f in ("decode_streamk.hip", "pa_mfma.h", "pa_device.h", "pa_launch.h")]
+KERNEL_NAMES = {
+    ("mfma", True): "pa_decode (pa_decode_streamk + pa_streamk_reduce)",
+    ("mfma", False): "pa_decode, explicit partitions (pa_decode_mfma + pa_splitk_reduce)",
+    ("valu", True): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
+    ("valu", False): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
+}
 
 
 def kernel_sources_sha256():
@@ -69,7 +75,8 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time the oracle baseline accumulates")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="0: pa_decode's balanced split (stream-K); else explicit partitions")
     ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
                     help="pa_decode (matrix-core kernel) or pa_decode_valu")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -175,7 +182,7 @@ def main():
                         "shuffled pool of blocks+10%",
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": b.num_kv_heads, "head_dim": d,
             "block_size": bs, "num_blocks": b.num_blocks, "max_blocks_per_seq": MB,
-            "partition_size": args.partition_size or 512, "kv_bytes": kv,
+            "partition_size": args.partition_size or "balanced (stream-K)", "kv_bytes": kv,
             "tokens": int(b.seq_lens.sum()),
         },
         "frac_of_hbm_peak": round(gbs_step / HBM_PEAK_GBS, 4),
@@ -183,8 +190,7 @@ def main():
         "decode_ms": round(ms_decode, 5),
         "decode_only_gbs": round(gbs_decode, 2),
         "roofline": {
-            "kernel": ("pa_decode (pa_decode_mfma + pa_splitk_reduce)" if args.impl == "mfma"
-                       else "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)"),
+            "kernel": KERNEL_NAMES[(args.impl, args.partition_size == 0)],
             "bound": "hbm",
             "achieved": round(gbs_decode, 2),
             "peak": HBM_PEAK_GBS,
@@ -193,11 +199,12 @@ def main():
             "traffic": None,
         },
     }
+    profiled = args.impl == "mfma" and args.partition_size == 0
     traffic, note = measured_traffic()
-    if args.impl == "mfma" and traffic is not None:
+    if profiled and traffic is not None:
         res["roofline"]["traffic"] = traffic
         res["roofline"]["traffic_over_algorithmic"] = round(traffic / kv, 4)
-    res["roofline"]["traffic_source"] = note if args.impl == "mfma" else "not profiled"
+    res["roofline"]["traffic_source"] = note if profiled else "not profiled"
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")

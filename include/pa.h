@@ -90,12 +90,16 @@ typedef enum pa_dtype {
  * Supported: dtype F16/BF16 (q, pools and out share it); head_dim 64 or
  * 128; block_size 8, 16 or 32; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  *
- * Long sequences are split into partitions of `partition_size` positions
- * (0 = automatic; otherwise a positive multiple of 16 and of block_size,
- * with at most 512 blocks per partition).  Each partition's softmax state is written to
- * `workspace` and merged by log-sum-exp in a second kernel.  The workspace
- * needs pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents
- * on entry do not matter and on return are unspecified.
+ * Work split.  partition_size = 0 (automatic) selects the balanced split:
+ * the (sequence, KV head) pairs are laid end to end as tiles of 16
+ * positions and every resident wave of the GPU takes an equal run of them;
+ * a pair cut between runs leaves partial softmax states that a second kernel
+ * merges by log-sum-exp.  partition_size > 0 (a multiple of 16 and of
+ * block_size, at most 512 blocks) selects fixed partitions of that many
+ * positions per (sequence, KV head), merged the same way.  Both give the
+ * same result up to float32 summation order.  The workspace needs
+ * pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents on
+ * entry do not matter and on return are unspecified.
  *
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, num_q_heads not a
  * multiple of num_kv_heads, bad partition_size, misaligned pointer),
@@ -112,7 +116,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * pa_decode computed by the wave-level vector kernel instead of the
  * matrix-core one: q.K as packed dot products reduced across the lanes of a
  * row, P.V as float32 FMAs.  Same arguments, contract, workspace and errors
- * as pa_decode; results agree to rounding (the two sum in different orders,
+ * as pa_decode, except that partition_size = 0 means fixed 512-position
+ * partitions; results agree to rounding (the two sum in different orders,
  * and this kernel keeps P in float32).
  */
 pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -123,10 +128,15 @@ pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const vo
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Workspace bytes pa_decode needs for these sizes: an upper bound computed
- * from max_blocks_per_seq * block_size (no device memory is read).  0 when no
- * sequence can need more than one partition, or when an argument is invalid
- * (pa_decode then reports the error).
+ * Workspace bytes pa_decode (and pa_decode_valu) need for these sizes; no
+ * device memory is read.  partition_size > 0: (m, l, acc) per (sequence,
+ * query head, partition), an upper bound from max_blocks_per_seq *
+ * block_size, 0 when no sequence can need more than one partition.
+ * partition_size = 0: the balanced split's partial states (two per wave, at
+ * most 8192 waves, min(num_q_heads, 8) heads each) and one 16-byte record
+ * per (sequence, query head), or the 512-position partitions
+ * pa_decode_valu uses in that mode, whichever is larger.  0 when an argument
+ * is invalid (pa_decode then reports the error).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_blocks_per_seq, int32_t block_size,

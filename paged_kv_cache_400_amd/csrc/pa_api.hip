@@ -39,6 +39,20 @@ int64_t partitions_needed(int32_t max_blocks_per_seq, int32_t block_size, int32_
   return (max_len + part - 1) / part;
 }
 
+// Workspace of the partitioned kernels: (m, l, acc) per (sequence, query
+// head, partition); 0 when no sequence can need more than one partition or
+// the partition size is invalid.
+size_t partitioned_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int32_t block_size,
+                                   int32_t partition_size) {
+  const int32_t part = resolve_partition(partition_size, block_size);
+  if (part == 0) return 0;
+  const int64_t pmax = partitions_needed(max_blocks_per_seq, block_size, part);
+  if (pmax <= 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * pmax;
+  return (size_t)(rows * head_dim * (int64_t)sizeof(float) + rows * 2 * (int64_t)sizeof(float));
+}
+
 bool supported_cache_dims(int32_t head_dim, int32_t block_size) {
   return head_dim >= 8 && head_dim <= 1024 && head_dim % 8 == 0 &&
          (block_size == 8 || block_size == 16 || block_size == 32);
@@ -69,12 +83,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0)
     return 0;
-  const int32_t part = resolve_partition(partition_size, block_size);
-  if (part == 0) return 0;
-  const int64_t pmax = partitions_needed(max_blocks_per_seq, block_size, part);
-  if (pmax <= 1) return 0;
-  const int64_t rows = (int64_t)num_seqs * num_q_heads * pmax;
-  return (size_t)(rows * head_dim * (int64_t)sizeof(float) + rows * 2 * (int64_t)sizeof(float));
+  const size_t part_bytes = partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                        max_blocks_per_seq, block_size,
+                                                        partition_size);
+  if (partition_size != 0) return part_bytes;
+  // automatic: pa_decode runs the balanced kernel, pa_decode_valu 512-position
+  // partitions; the workspace serves either
+  const size_t sk = (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim);
+  return sk > part_bytes ? sk : part_bytes;
 }
 
 }  // extern "C"
@@ -125,13 +141,45 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
   if (units * 256 >= kMaxThreadsPerLaunch || pmax > INT32_MAX)
     return fail(PA_ERR_SHAPE, "pa_decode: %lld work units exceed one launch",
                 (long long)units);
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                max_blocks_per_seq, block_size, partition_size);
+  const bool balanced = impl == Impl::kMfma && partition_size == 0;
+  const size_t need =
+      balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim)
+               : partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                             block_size, partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
   if (need > 0 && !aligned16(workspace))
     return fail(PA_ERR_SHAPE, "pa_decode: workspace must be 16-byte aligned");
+
+  if (balanced) {
+    pa::StreamKArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    char* ws = (char*)workspace;
+    a.ws_acc = (float*)ws;
+    a.ws_ml = (float2*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim));
+    a.ws_meta = (int4*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim) +
+                        pa::streamk_ml_bytes(num_q_heads));
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.qk_scale = scale * 1.4426950408889634f;
+    a.bf16 = dtype == PA_BF16;
+    a.stream = stream;
+    const hipError_t e = pa::launch_decode_streamk(a);
+    if (e != hipSuccess)
+      return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+  }
 
   pa::DecodeArgs a;
   a.out = out;

@@ -23,6 +23,43 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+// Balanced (stream-K) decode (decode_streamk.hip), pa_decode's automatic
+// mode.  Workspace: ws_acc float [2 * kStreamKMaxWaves][Gmax][D], then ws_ml
+// float2 [2 * kStreamKMaxWaves][Gmax], then ws_meta int4 [S * Hkv], with
+// Gmax = min(Hq, 8); streamk_workspace_bytes gives the total.
+constexpr int kStreamKMaxWaves = 8192;
+
+struct StreamKArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_acc;
+  float2* ws_ml;
+  int4* ws_meta;
+  int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq, num_blocks;
+  float qk_scale;
+  bool bf16;
+  hipStream_t stream;
+};
+
+inline int64_t streamk_gmax(int32_t num_q_heads) { return num_q_heads < 8 ? num_q_heads : 8; }
+inline int64_t streamk_acc_bytes(int32_t num_q_heads, int32_t head_dim) {
+  return 2 * (int64_t)kStreamKMaxWaves * streamk_gmax(num_q_heads) * head_dim * 4;
+}
+inline int64_t streamk_ml_bytes(int32_t num_q_heads) {
+  return 2 * (int64_t)kStreamKMaxWaves * streamk_gmax(num_q_heads) * 8;
+}
+inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+  return streamk_acc_bytes(num_q_heads, head_dim) + streamk_ml_bytes(num_q_heads) +
+         (int64_t)num_seqs * num_q_heads * 16;
+}
+
+hipError_t launch_decode_streamk(const StreamKArgs& a);
+
 // pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
 // (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.
 hipError_t launch_decode(const DecodeArgs& a);

@@ -1,0 +1,237 @@
+// pa_mfma.h -- the per-wave machinery of the matrix-core decode kernels
+// (gfx950): MFMA wrappers, the LDS layout of a V tile, and TileWave, which
+// loads and consumes tiles of 16 positions x G query heads.
+//
+// A tile of 16 positions (one KV head) is handled as follows:
+//
+//  loads   K goes to registers, V goes straight from HBM into the wave's LDS
+//          tile (global_load_lds_dwordx4, no VGPRs), both with the streaming
+//          (nt) hint.  The caller issues a tile one step ahead of consuming
+//          it.  A position past the end of the range is clamped to the last
+//          valid one (so no unused slot is ever read) and its score masked.
+//  q.K^T   S[t][h] = sum_d K[t][d] q[h][d] as D/32 v_mfma_f32_16x16x32
+//          (A = K rows: lane l holds 16 bytes of position l%16; B = q:
+//          lane l holds the same 16 bytes of head l%16, zero for l%16 >= G).
+//          The d-chunk of lane l at step c is c*4 + l/16, so a load
+//          instruction reads 64 contiguous bytes of each of 16 rows.  No
+//          cross-lane reduction: lane l receives head l%16's scores for
+//          positions 4*(l/16)+r, r = 0..3.
+//  softmax scores in base 2 (scale * log2 e folded in).  The running max of
+//          a head is raised only when a score exceeds it by more than 8
+//          (then every weight stays <= 2^8); that test is a wave-wide
+//          ballot, so the usual tile needs no lane exchange and no rescale.
+//  P.V     acc[h][d] += sum_t P[h][t] V[t][d] as D/16 v_mfma_f32_16x16x16
+//          (A = P: the q.K^T result is already in the A layout; B = V with
+//          the 16 positions along k, read column-wise from LDS as 16-bit
+//          values).  The V tile is stored as four 4-row regions, each
+//          padded by 32 bytes, so the four lane groups of a read hit
+//          disjoint LDS banks and every read address is a lane base plus an
+//          immediate offset.
+//  P is rounded to the input type for the P.V product and the softmax
+//  denominator sums the same rounded weights.  MFMA rows for heads >= G
+//  compute on zero queries and are never written.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+constexpr int kTile = 16;             // positions per tile
+constexpr float kRescaleSlack = 8.0f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T> __device__ __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c);
+template <> __device__ __forceinline__ f32x4_t mfma_k32<BF16>(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4_t mfma_k32<F16>(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c);
+template <> __device__ __forceinline__ f32x4_t mfma_k16<BF16>(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4_t mfma_k16<F16>(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                               __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> two 16-bit values packed in one word (round to nearest even).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
+template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+}
+
+// s_waitcnt vmcnt(0): every outstanding vector-memory load of this wave,
+// the copies of V into LDS included, has landed.  The empty asm with a memory
+// clobber keeps the compiler from moving LDS reads above the wait or the next
+// LDS copies above the previous tile's reads.
+__device__ __forceinline__ void wait_vmem_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0, expcnt 7, lgkmcnt 15
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+struct Geo {
+  static constexpr int KC = D / 32;                 // q.K^T MFMA steps
+  static constexpr int NM = D / 16;                 // P.V MFMAs
+  static constexpr int ROW = D * 2;                 // bytes of one V row
+  static constexpr int REGION = 4 * ROW + 32;       // 4 rows + padding
+  static constexpr int TILE = 4 * REGION;           // one LDS V tile
+  static constexpr int LANES = 4 * ROW / 16;        // lanes that fill a region
+};
+
+// One wave's softmax state for the G query heads of one KV head, and the
+// loading and consuming of its tiles.  vtile points at the wave's two LDS V
+// tiles (2 * Geo<D>::TILE bytes).
+template <typename T, int D, int BS, int G>
+struct TileWave {
+  using GE = Geo<D>;
+  static constexpr int KC = GE::KC, NM = GE::NM;
+  static_assert(G <= 16, "one MFMA row per query head");
+
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int64_t blk_stride;  // elements per block of a pool
+  int64_t head_off;    // elements to the KV head within a block
+  unsigned char* vtile;
+  int lane, col, grp;
+
+  uint4 qb[KC];      // q operand (B of q.K^T): head col, d-chunk c*4 + grp
+  f32x4_t acc[NM];   // P.V accumulators: head 4*grp + r, column 16*m + col
+  float m_run;       // running max of head col (same in the 4 lane groups)
+  float l_run;       // this lane's share of head col's denominator
+
+  __device__ __forceinline__ void init(const uint16_t* kc_, const uint16_t* vc_, int hkv, int kh,
+                                       unsigned char* vtile_) {
+    kc = kc_;
+    vc = vc_;
+    blk_stride = (int64_t)hkv * BS * D;
+    head_off = (int64_t)kh * BS * D;
+    vtile = vtile_;
+    lane = threadIdx.x & 63;
+    col = lane & 15;
+    grp = lane >> 4;
+  }
+
+  // q rows of the G heads start at q_rows ([G][D]); zero operand for col >= G.
+  __device__ __forceinline__ void load_q(const uint16_t* q_rows) {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      qb[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (col < G) qb[c] = *reinterpret_cast<const uint4*>(q_rows + col * D + (c * 4 + grp) * 8);
+    }
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = kNegInf;
+    l_run = 0.0f;
+  }
+
+  // Issue the K (to registers kr) and V (to LDS buffer `buf`) loads of the
+  // tile at positions t0..t0+15, clamped to t_last.  id0 is the block of t0;
+  // for blocks of 8 positions id1 is the block of t0 + 8.
+  __device__ __forceinline__ void issue(uint4 (&kr)[KC], int buf, int t0, int t_last, int id0,
+                                        int id1) {
+    const uint16_t* kb0 = kc + (int64_t)id0 * blk_stride + head_off;
+    const uint16_t* kb1 = kc + (int64_t)id1 * blk_stride + head_off;
+    const uint16_t* vb0 = vc + (int64_t)id0 * blk_stride + head_off;
+    const uint16_t* vb1 = vc + (int64_t)id1 * blk_stride + head_off;
+    // K: position col (clamped), chunk c*4 + grp
+    {
+      const int t = min(t0 + col, t_last);
+      const uint16_t* kr_base = (BS < kTile && t - t0 >= BS) ? kb1 : kb0;
+      const uint16_t* ptr = kr_base + (t % BS) * D + grp * 8;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kr[c] = load_stream(ptr + c * 32);
+    }
+    // V: region i holds rows 4i..4i+3; lane l (< LANES) loads row 4i + l/(D/8),
+    // chunk l%(D/8), landing at region i + 16*l bytes
+    unsigned char* vt = vtile + buf * GE::TILE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = 4 * i + lane / (D / 8);
+      const int t = min(t0 + tau, t_last);
+      const uint16_t* vrow = ((BS < kTile && t - t0 >= BS) ? vb1 : vb0) + (t % BS) * D;
+      if (GE::LANES == 64 || lane < GE::LANES)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vrow + (lane % (D / 8)) * 8),
+            (void __attribute__((address_space(3)))*)(vt + i * GE::REGION), 16, 0,
+            kCachePolicyStream);
+    }
+  }
+
+  // Compute the tile at t0 (positions >= t_end masked) whose K is in kr and
+  // V in LDS buffer `buf`.
+  __device__ __forceinline__ void consume(const uint4 (&kr)[KC], int buf, int t0, int t_end,
+                                          float qk_scale) {
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) sc = mfma_k32<T>(kr[c], qb[c], sc);
+
+    float sr[4];
+    float lm = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sr[r] = (t0 + 4 * grp + r < t_end) ? sc[r] * qk_scale : kNegInf;
+      lm = fmaxf(lm, sr[r]);
+    }
+    if (__builtin_amdgcn_ballot_w64(lm > m_run + kRescaleSlack) != 0) {
+      float mx = fmaxf(lm, __shfl_xor(lm, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = exp2_fast(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= corr;
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
+      }
+    }
+    const uint32_t p01 = pack2<T>(exp2_fast(sr[0] - m_run), exp2_fast(sr[1] - m_run));
+    const uint32_t p23 = pack2<T>(exp2_fast(sr[2] - m_run), exp2_fast(sr[3] - m_run));
+    l_run += (lo_f32<T>(p01) + hi_f32<T>(p01)) + (lo_f32<T>(p23) + hi_f32<T>(p23));
+    const uint2 pa_op = make_uint2(p01, p23);
+
+    // B operand: V[4*grp + r][16*m + col] from region grp, row r
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(vtile + buf * GE::TILE +
+                                                           grp * GE::REGION) + col;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint32_t b0 = vr[0 * D + 16 * m];
+      const uint32_t b1 = vr[1 * D + 16 * m];
+      const uint32_t b2 = vr[2 * D + 16 * m];
+      const uint32_t b3 = vr[3 * D + 16 * m];
+      acc[m] = mfma_k16<T>(pa_op, make_uint2(b0 | (b1 << 16), b2 | (b3 << 16)), acc[m]);
+    }
+  }
+
+  // After the last tile: every lane holds head col's whole denominator.
+  __device__ __forceinline__ void finish() {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+  }
+};
+
+}  // namespace pa
