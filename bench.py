@@ -15,7 +15,9 @@ Prints one JSON line:
               once; tail slots of partial blocks not counted)
   roofline    pa_decode's achieved B_kv / (mean duration of its launches,
               HIP events on its stream over the timed steps) against the
-              8 TB/s HBM peak
+              8 TB/s HBM peak; `achievable` is the same figure for
+              pa_probe_gather, which issues exactly pa_decode's K/V loads and
+              computes nothing (the gather pattern's own ceiling)
   cpu_baseline  the float64 CPU oracle on the same step, host cores
 """
 import argparse
@@ -73,6 +75,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--ceiling", choices=["on", "off"], default="on",
+                    help="also time pa_probe_gather (the same loads, no arithmetic)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time the oracle baseline accumulates")
     ap.add_argument("--partition-size", type=int, default=0,
@@ -160,6 +164,22 @@ def main():
     ms_step = start.elapsed_time(end) / K
     ms_decode = sum(a.elapsed_time(z) for a, z in ev) / K
 
+    # the access pattern's own ceiling: the same K/V loads, nothing computed
+    ceiling = None
+    if args.ceiling == "on":
+        for _ in range(args.warmup):
+            pa.probe_gather(dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
+                            Hq)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
+        for _ in range(K):
+            pa.probe_gather(dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
+                            Hq)
+        c1.record()
+        torch.cuda.synchronize()
+        ceiling = c0.elapsed_time(c1) / K
+
     kv = b.kv_bytes()
     gbs_step = kv / (ms_step * 1e-3) / 1e9
     gbs_decode = kv / (ms_decode * 1e-3) / 1e9
@@ -199,6 +219,15 @@ def main():
             "traffic": None,
         },
     }
+    if ceiling is not None:
+        gbs_ceiling = kv / (ceiling * 1e-3) / 1e9
+        res["roofline"]["achievable"] = {
+            "kernel": "pa_probe_gather: the same grid and K/V loads as pa_decode's balanced split, "
+                      "no arithmetic",
+            "us": round(ceiling * 1e3, 2), "gbs": round(gbs_ceiling, 2),
+            "frac_of_peak": round(gbs_ceiling / HBM_PEAK_GBS, 4),
+            "decode_frac_of_achievable": round(gbs_decode / gbs_ceiling, 4),
+        }
     profiled = args.impl == "mfma" and args.partition_size == 0
     traffic, note = measured_traffic()
     if profiled and traffic is not None:

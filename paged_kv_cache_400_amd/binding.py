@@ -19,7 +19,7 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_H
 PA_F16, PA_BF16 = 0, 1
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
-# (name, restype, argtypes) for every entry point of include/pa.h
+# (name, restype, argtypes) for every entry point of include/pa.h and include/pa_probe.h
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -31,6 +31,8 @@ SIGNATURES = {
                                             _i32, ctypes.c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.c_int, _vp]),
+    "pa_probe_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, ctypes.c_int, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (ctypes.c_int32, []),
@@ -178,3 +180,24 @@ def copy_blocks(k_cache, v_cache, block_mapping):
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                block_mapping.shape[0], Hkv, d, bs, NB, _DT[k_cache.dtype],
                                _stream(dev)))
+
+
+def probe_gather(k_cache, v_cache, block_tables, seq_lens, num_q_heads, sink=None):
+    """Measurement support (include/pa_probe.h): read exactly the K/V bytes
+    pa_decode's balanced split reads, with the same loads, computing nothing.
+    Returns the sink tensor (2 int16 words on the pools' device)."""
+    _need(k_cache, "k_cache", 4)
+    dev = k_cache.device
+    if k_cache.dtype not in _DT:
+        raise ValueError(f"k_cache must be float16 or bfloat16, got {k_cache.dtype}")
+    _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    NB, Hkv, bs, d = k_cache.shape
+    S, MB = block_tables.shape
+    if sink is None:
+        sink = torch.zeros(2, dtype=torch.int16, device=dev)
+    _check(_lib.pa_probe_gather(_ptr(sink), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                _ptr(seq_lens), S, num_q_heads, Hkv, d, bs, MB, NB,
+                                _DT[k_cache.dtype], _stream(dev)))
+    return sink

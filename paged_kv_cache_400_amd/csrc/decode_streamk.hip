@@ -68,8 +68,12 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 
 }  // namespace
 
-template <typename T, int D, int BS, int G>
-__global__ void __launch_bounds__(kThreads)
+// kGather = true is the gather-only instantiation behind pa_probe_gather:
+// the same split, walk and K/V loads, no q, no arithmetic on the data and no
+// results (a word is written to `out` only if the XOR of the loaded data hits
+// a value it cannot be expected to hit).
+template <typename T, int D, int BS, int G, bool kGather>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   float2* __restrict__ ws_ml, int4* __restrict__ ws_meta,
                   const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -126,6 +130,46 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   int kh = (int)((g0 - seq_start) / ns);
   int t_lo = (int)((g0 - seq_start) % ns);
 
+  // The segment's result: final rows for a pair wholly inside the run, else
+  // a partial in slot 0 (the run's first pair) or 1 (its last); the wave
+  // holding a pair's last tile records where its partials are.
+  auto write_result = [&](const TileWave<T, D, BS, G>& t, bool bad, int64_t row0, int t_lo,
+                          int t_hi, int ns, bool first, int64_t pair_start) {
+    const int col = lane & 15, grp = lane >> 4;
+    if (t_lo == 0 && t_hi == ns) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        const float l_h = __shfl(t.l_run, h);
+        if (h < G) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const float v = bad ? __builtin_nanf("") : t.acc[m][r] / l_h;
+            out[(row0 + h) * D + 16 * m + col] = to_bits<T>(v);
+          }
+        }
+      }
+    } else {
+      const int64_t slot = (int64_t)wave * 2 + (first ? 0 : 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+            ws_acc[(slot * G + h) * D + 16 * m + col] = bad ? __builtin_nanf("") : t.acc[m][r];
+        }
+      }
+      if (lane < G)
+        ws_ml[slot * G + lane] = make_float2(t.m_run, bad ? __builtin_nanf("") : t.l_run);
+    }
+    if (t_hi == ns && lane == 0) {
+      const int c_first = (int)(pair_start / chunk);
+      const int c_last = (int)((pair_start + ns - 1) / chunk);
+      ws_meta[row0 / G] = make_int4(c_first, c_last, pair_start % chunk != 0, 0);
+    }
+  };
+
   TileWave<T, D, BS, G> tw;
   unsigned char* vtile = s_mem + w * 2 * GE::TILE;
 
@@ -141,8 +185,17 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     const int32_t* bt_row = block_tables + (int64_t)s * mb;
 
     tw.init(kc, vc, hkv, kh, vtile);
-    tw.load_q(q + row0 * D);
+    if constexpr (!kGather) tw.load_q(q + row0 * D);
     tw.reset();
+    uint32_t gathered = 0;
+    auto consume = [&](const uint4 (&kr)[KC], int buf, int t0) {
+      if constexpr (kGather) {
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vtile + buf * GE::TILE);
+        gathered ^= kr[0].x ^ kr[KC - 1].w ^ vw[lane];
+      } else {
+        tw.consume(kr, buf, t0, p_end, qk_scale);
+      }
+    };
 
     // block ids of the segment, 64 at a time: lane j holds block blk_base + j
     const int blk_last = (p_end - 1) / BS;
@@ -181,49 +234,18 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     for (int j = 0;;) {
       wait_vmem_all();
       if (j + 1 < ntiles) issue(kb, 1, j + 1);
-      tw.consume(ka, 0, p_lo + j * kTile, p_end, qk_scale);
+      consume(ka, 0, p_lo + j * kTile);
       if (++j >= ntiles) break;
       wait_vmem_all();
       if (j + 1 < ntiles) issue(ka, 0, j + 1);
-      tw.consume(kb, 1, p_lo + j * kTile, p_end, qk_scale);
+      consume(kb, 1, p_lo + j * kTile);
       if (++j >= ntiles) break;
     }
-    tw.finish();
-
-    // ---- the segment's result: final rows, or a partial
-    const int col = lane & 15, grp = lane >> 4;
-    const bool whole = t_lo == 0 && t_hi == ns;
-    if (whole) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        const float l_h = __shfl(tw.l_run, h);
-        if (h < G) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const float v = bad ? __builtin_nanf("") : tw.acc[m][r] / l_h;
-            out[(row0 + h) * D + 16 * m + col] = to_bits<T>(v);
-          }
-        }
-      }
+    if constexpr (kGather) {
+      if (gathered == 0x9e3779b9u && lane == 0) out[0] = (uint16_t)gathered;
     } else {
-      const int64_t slot = (int64_t)wave * 2 + (g == g0 ? 0 : 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        if (h < G) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-            ws_acc[(slot * G + h) * D + 16 * m + col] = bad ? __builtin_nanf("") : tw.acc[m][r];
-        }
-      }
-      if (lane < G)
-        ws_ml[slot * G + lane] = make_float2(tw.m_run, bad ? __builtin_nanf("") : tw.l_run);
-    }
-    if (t_hi == ns && lane == 0) {  // this wave holds the pair's last tile
-      const int c_first = (int)(pair_start / chunk);
-      const int c_last = (int)((pair_start + ns - 1) / chunk);
-      ws_meta[(int64_t)s * hkv + kh] = make_int4(c_first, c_last, pair_start % chunk != 0, 0);
+      tw.finish();
+      write_result(tw, bad, row0, t_lo, t_hi, ns, g == g0, pair_start);
     }
 
     g += ntiles;
@@ -287,7 +309,7 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
 // device; recomputing it gives the same value, so concurrent first calls are
 // harmless).
 template <typename K>
-static int resident_waves(K kernel) {
+static int resident_waves(K* kernel) {
   constexpr int kMaxDevices = 64;
   static int cache[kMaxDevices];
   int dev = 0;
@@ -305,16 +327,23 @@ static int resident_waves(K kernel) {
 }
 
 template <typename T, int D, int BS, int G>
-static hipError_t launch_t(const StreamKArgs& a) {
-  auto kernel = pa_decode_streamk<T, D, BS, G>;
-  int waves = resident_waves(kernel);
+static hipError_t launch_t(const StreamKArgs& a, bool gather) {
+  int waves = resident_waves(pa_decode_streamk<T, D, BS, G, false>);
   if (waves <= 0) return hipErrorInvalidDevice;
-  waves = min(waves, kStreamKMaxWaves);
-  hipLaunchKernelGGL(kernel, dim3((uint32_t)(waves / kWaves)), dim3(kThreads), 0, a.stream,
-                     (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                     a.seq_lens, a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks,
-                     (waves / kWaves) * kWaves, a.qk_scale);
+  waves = min(waves, kStreamKMaxWaves) / kWaves * kWaves;
+  if (gather) {  // the same grid, gather-only (the group does not change the loads)
+    hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, 1, true>), dim3((uint32_t)(waves / kWaves)),
+                       dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
+                       nullptr, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,
+                       a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
+                       a.max_blocks_per_seq, a.num_blocks, waves, 0.0f);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false>), dim3((uint32_t)(waves / kWaves)),
+                     dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                     (const uint16_t*)a.v_cache, a.block_tables, a.seq_lens, a.num_seqs,
+                     a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, waves, a.qk_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pa_streamk_reduce<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),
@@ -324,37 +353,41 @@ static hipError_t launch_t(const StreamKArgs& a) {
 }
 
 template <typename T, int D, int BS>
-static hipError_t launch_g(const StreamKArgs& a) {
+static hipError_t launch_g(const StreamKArgs& a, bool gather) {
   switch (a.group) {
-    case 1: return launch_t<T, D, BS, 1>(a);
-    case 2: return launch_t<T, D, BS, 2>(a);
-    case 4: return launch_t<T, D, BS, 4>(a);
-    case 8: return launch_t<T, D, BS, 8>(a);
+    case 1: return launch_t<T, D, BS, 1>(a, gather);
+    case 2: return launch_t<T, D, BS, 2>(a, gather);
+    case 4: return launch_t<T, D, BS, 4>(a, gather);
+    case 8: return launch_t<T, D, BS, 8>(a, gather);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
-static hipError_t launch_bs(const StreamKArgs& a) {
+static hipError_t launch_bs(const StreamKArgs& a, bool gather) {
   switch (a.block_size) {
-    case 8: return launch_g<T, D, 8>(a);
-    case 16: return launch_g<T, D, 16>(a);
-    case 32: return launch_g<T, D, 32>(a);
+    case 8: return launch_g<T, D, 8>(a, gather);
+    case 16: return launch_g<T, D, 16>(a, gather);
+    case 32: return launch_g<T, D, 32>(a, gather);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t launch_d(const StreamKArgs& a) {
+static hipError_t launch_d(const StreamKArgs& a, bool gather) {
   switch (a.head_dim) {
-    case 64: return launch_bs<T, 64>(a);
-    case 128: return launch_bs<T, 128>(a);
+    case 64: return launch_bs<T, 64>(a, gather);
+    case 128: return launch_bs<T, 128>(a, gather);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_streamk(const StreamKArgs& a) {
-  return a.bf16 ? launch_d<BF16>(a) : launch_d<F16>(a);
+  return a.bf16 ? launch_d<BF16>(a, false) : launch_d<F16>(a, false);
+}
+
+hipError_t launch_gather_streamk(const StreamKArgs& a) {
+  return a.bf16 ? launch_d<BF16>(a, true) : launch_d<F16>(a, true);
 }
 
 }  // namespace pa

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include "pa.h"
+#include "pa_probe.h"
 #include "pa_launch.h"
 
 namespace {
@@ -299,6 +300,54 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                                               stream);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "pa_probe_gather: sizes must be positive (num_seqs >= 0)");
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_probe_gather: dtype %d not supported", (int)dtype);
+  if ((head_dim != 64 && head_dim != 128) ||
+      (block_size != 8 && block_size != 16 && block_size != 32))
+    return fail(PA_ERR_UNSUPPORTED, "pa_probe_gather: head_dim %d or block_size %d not built",
+                head_dim, block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "pa_probe_gather: num_q_heads %d is not a multiple of %d",
+                num_q_heads, num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_probe_gather: query group %d not in {1, 2, 4, 8}",
+                group);
+  if (num_seqs == 0) return PA_OK;
+  if (!sink || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "pa_probe_gather: a required pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE, "pa_probe_gather: k_cache and v_cache must be 16-byte aligned");
+  pa::StreamKArgs a = {};
+  a.out = sink;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.bf16 = dtype == PA_BF16;
+  a.stream = stream;
+  const hipError_t e = pa::launch_gather_streamk(a);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_probe_gather: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

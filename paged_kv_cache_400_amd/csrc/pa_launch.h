@@ -59,6 +59,9 @@ inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 hipError_t launch_decode_streamk(const StreamKArgs& a);
+// Gather-only run of the same split and loads (pa_probe_gather); uses only
+// out (a sink word), the pools, block_tables, seq_lens and the sizes.
+hipError_t launch_gather_streamk(const StreamKArgs& a);
 
 // pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
 // (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.

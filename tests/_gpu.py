@@ -5,6 +5,15 @@ Tolerance for attention outputs (fp16/bf16 inputs, float32 accumulation,
 output rounded to the input dtype): max-abs <= 1e-2 and mean-abs <= 1e-3
 against the float64 oracle.  Pools after the append and the copy are
 compared bit for bit.
+
+The plain max-abs bound cannot hold for every input: a result whose
+magnitude is 4 or more is, in bfloat16, 2^-5 apart from its neighbours, so
+even the correctly rounded value can miss the float64 one by 2^-6 = 0.0156.
+The five workloads (values N(0, 1), sequences of 3 positions or more) keep
+outputs well below that and are held to the plain bound.  Stress inputs
+whose outputs can be large (many sequences of one or two positions) are held
+to it beyond half a unit in the last place of the output type
+(``round_slack=True``); the mean-abs bound is unchanged.
 """
 import numpy as np
 import torch
@@ -52,7 +61,20 @@ def gpu_bits(t):
     return bits(t.cpu())
 
 
-def compare(out_gpu, ref, pairs=None, label=""):
+# significand bits after the point, smallest normal exponent
+_FORMAT = {torch.bfloat16: (7, -126), torch.float16: (10, -14)}
+
+
+def half_ulp(ref, dtype):
+    """Half a unit in the last place of ``dtype`` at each value of ``ref``."""
+    bits, emin = _FORMAT[dtype]
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(np.where(a > 0, e, emin), emin)
+    return np.ldexp(0.5, (e - bits).astype(np.int64))
+
+
+def compare(out_gpu, ref, pairs=None, label="", round_slack=False):
     """Assert the attention tolerance; returns (max_abs, mean_abs)."""
     got = out_gpu.detach().double().cpu().numpy()
     if pairs is not None:
@@ -61,7 +83,10 @@ def compare(out_gpu, ref, pairs=None, label=""):
     assert np.isfinite(ref).all(), "oracle produced non-finite values"
     assert np.isfinite(got).all(), f"{label}: GPU output has non-finite values"
     err = np.abs(got - ref)
-    mx, mean = float(err.max()), float(err.mean())
+    mean = float(err.mean())
+    if round_slack:
+        err = np.maximum(err - half_ulp(ref, out_gpu.dtype), 0.0)
+    mx = float(err.max())
     assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{label}: max-abs {mx:.3g} mean-abs {mean:.3g}"
     return mx, mean
 

@@ -14,6 +14,7 @@ import torch  # noqa: F401  (loads torch's HIP runtime first, as the binding doe
 from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "pa_probe.h")]
 LIB = os.path.join(ROOT, "paged_kv_cache_400_amd", "libpa.so")
 
 
@@ -27,9 +28,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():

@@ -1,0 +1,108 @@
+"""GPU parity of pa_decode's two ways of cutting the work, on the inputs that
+stress them, against the float64 CPU oracle (max-abs <= 1e-2, mean-abs <=
+1e-3; pools after the append bit-exact):
+
+  * the balanced split (partition_size 0): many short sequences, so one wave
+    walks dozens of (sequence, head) pairs and the prefix search over the
+    sequences crosses several 64-sequence chunks; one long sequence on one KV
+    head, cut across hundreds of waves, so the merge combines hundreds of
+    partials; empty sequences between non-empty ones;
+  * fixed partitions (partition_size > 0) on the same inputs;
+  * contract violations the kernels guard against (a length past the block
+    table, a block id outside the pool): that sequence's rows are NaN, no
+    other row changes.
+Outputs of sequences of one or two positions can be large, so the max-abs
+bound is applied beyond half an ulp of the output type (see _gpu.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_400_amd as pa
+from _gpu import compare, gpu_bits, gpu_step, oracle_out, oracle_pools
+from paged_kv_cache_400_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = [0, 64, 512]
+
+
+def _lens_many_short():
+    rng = np.random.default_rng(11)
+    return rng.integers(0, 40, 300).tolist()  # zeros included
+
+
+@pytest.mark.parametrize("part", SPLITS)
+def test_many_short_sequences(part):
+    b = wl.make_decode_batch("many_short", _lens_many_short(), 32, 8, 128, 16, "bf16", seed=21,
+                             append=1)
+    out, dev = gpu_step(b, partition_size=part)
+    kp, vp = oracle_pools(b)
+    assert np.array_equal(gpu_bits(dev["k_cache"]), kp)
+    compare(out, oracle_out(b, kp, vp), label=f"many_short part{part}", round_slack=True)
+
+
+@pytest.mark.parametrize("part", SPLITS)
+@pytest.mark.parametrize("bs", [8, 32])
+def test_one_long_sequence_one_kv_head(part, bs):
+    b = wl.make_decode_batch("one_long", [20000], 8, 1, 128, bs, "bf16", seed=22, append=1)
+    out, dev = gpu_step(b, partition_size=part)
+    kp, vp = oracle_pools(b)
+    compare(out, oracle_out(b, kp, vp), label=f"one_long bs{bs} part{part}", round_slack=True)
+
+
+@pytest.mark.parametrize("part", SPLITS)
+def test_empty_sequences_between_long_ones(part):
+    lens = [0, 3000, 0, 0, 1, 0, 4500, 0]
+    b = wl.make_decode_batch("gaps", lens, 16, 4, 64, 16, "f16", seed=23, append=0)
+    out, dev = gpu_step(b, partition_size=part)
+    kp, vp = oracle_pools(b)
+    ref = oracle_out(b, kp, vp)
+    compare(out, ref, label=f"gaps part{part}", round_slack=True)
+    got = out.float().cpu().numpy()
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[s] == 0.0)
+
+
+def _violation_batch():
+    return wl.make_decode_batch("violation", [700, 33, 1500, 90, 16], 16, 4, 128, 16, "bf16",
+                                seed=24, append=0)
+
+
+@pytest.mark.parametrize("part", SPLITS)
+@pytest.mark.parametrize("what", ["length", "block_id"])
+def test_contract_violation_gives_nan_rows_of_that_sequence_only(part, what):
+    b = _violation_batch()
+    dev = wl.to_device(b, "cuda:0")
+    bad = 2
+    if what == "length":  # longer than its block table holds
+        lens = dev["seq_lens"].clone()
+        lens[bad] = b.max_blocks_per_seq * b.block_size + 1
+        dev["seq_lens"] = lens
+    else:  # a live entry of its block table points past the pool
+        bt = dev["block_tables"].clone()
+        bt[bad, 1] = b.num_blocks + 7
+        dev["block_tables"] = bt
+    out = pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                    dev["seq_lens"], scale=b.scale, partition_size=part)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.all(np.isnan(got[bad])), "the violating sequence's rows must be NaN"
+    keep = [s for s in range(b.num_seqs) if s != bad]
+    pairs = np.array([(s, h) for s in keep for h in range(b.num_q_heads)], np.int32)
+    ref = oracle_out(b, wl.bits(b.k_cache), wl.bits(b.v_cache), pairs=pairs)
+    compare(out, ref, pairs=pairs, label=f"violation {what} part{part}", round_slack=True)
+
+
+def test_balanced_and_partitioned_agree_on_the_mixed_step():
+    b = wl.make_mixed_step()
+    out0, dev = gpu_step(b, partition_size=0)
+    out512 = pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                       dev["seq_lens"], scale=b.scale, partition_size=512)
+    torch.cuda.synchronize()
+    # both are within the oracle tolerance (the full-size test checks that);
+    # between themselves they differ only by float32 order and one bf16 ulp
+    diff = (out0.float() - out512.float()).abs()
+    assert torch.isfinite(diff).all()
+    assert float(diff.max()) <= 1e-2
