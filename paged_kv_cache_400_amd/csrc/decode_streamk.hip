@@ -132,34 +132,42 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 
   // The segment's result: final rows for a pair wholly inside the run, else
   // a partial in slot 0 (the run's first pair) or 1 (its last); the wave
-  // holding a pair's last tile records where its partials are.
+  // holding a pair's last tile records where its partials are.  The G x D
+  // result leaves the MFMA layout 64 bytes per head row at a time, so it is
+  // staged row-major in the wave's V tiles (idle once the last tile is
+  // consumed) and stored 16 bytes per lane: whole, contiguous cache lines.
+  // (Stores of 32 or 64 bytes per instruction cost the mixed decode step 2%.)
   auto write_result = [&](const TileWave<T, D, BS, G>& t, bool bad, int64_t row0, int t_lo,
                           int t_hi, int ns, bool first, int64_t pair_start) {
     const int col = lane & 15, grp = lane >> 4;
-    if (t_lo == 0 && t_hi == ns) {
+    const bool whole = t_lo == 0 && t_hi == ns;
+    float* st = reinterpret_cast<float*>(t.vtile);  // [G][D]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        const float l_h = __shfl(t.l_run, h);
-        if (h < G) {
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * grp + r;
+      const float l_h = __shfl(t.l_run, h);
+      if (h < G) {
 #pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const float v = bad ? __builtin_nanf("") : t.acc[m][r] / l_h;
-            out[(row0 + h) * D + 16 * m + col] = to_bits<T>(v);
-          }
+        for (int m = 0; m < NM; ++m) {
+          const float v = whole ? t.acc[m][r] / l_h : t.acc[m][r];
+          st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : v;
         }
+      }
+    }
+    // one wave's LDS accesses take effect in program order
+    if (whole) {
+      for (int i = lane * 8; i < G * D; i += 64 * 8) {
+        const float4 a = *reinterpret_cast<const float4*>(st + i);
+        const float4 b = *reinterpret_cast<const float4*>(st + i + 4);
+        *reinterpret_cast<uint4*>(out + row0 * D + i) =
+            make_uint4(pack2<T>(a.x, a.y), pack2<T>(a.z, a.w), pack2<T>(b.x, b.y),
+                       pack2<T>(b.z, b.w));
       }
     } else {
       const int64_t slot = (int64_t)wave * 2 + (first ? 0 : 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        if (h < G) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-            ws_acc[(slot * G + h) * D + 16 * m + col] = bad ? __builtin_nanf("") : t.acc[m][r];
-        }
-      }
+      for (int i = lane * 4; i < G * D; i += 64 * 4)
+        *reinterpret_cast<float4*>(ws_acc + slot * G * D + i) =
+            *reinterpret_cast<const float4*>(st + i);
       if (lane < G)
         ws_ml[slot * G + lane] = make_float2(t.m_run, bad ? __builtin_nanf("") : t.l_run);
     }
@@ -169,6 +177,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       ws_meta[row0 / G] = make_int4(c_first, c_last, pair_start % chunk != 0, 0);
     }
   };
+  static_assert(sizeof(float) * G * D <= 2 * GE::TILE, "the result fits the wave's V tiles");
 
   TileWave<T, D, BS, G> tw;
   unsigned char* vtile = s_mem + w * 2 * GE::TILE;
