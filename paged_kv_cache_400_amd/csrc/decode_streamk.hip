@@ -275,41 +275,67 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 // Merge of the partials of every (sequence, KV head) pair split between
 // waves, plus the rows no wave writes: zero rows for empty sequences, NaN
 // rows for lengths outside [0, max_blocks_per_seq * block_size].  One
-// workgroup per pair, one thread per (query head, element).
+// workgroup per pair; a thread merges 4 consecutive elements of one query
+// head.  The length and the pair's record are loaded together, then the
+// partials four at a time with all their loads in flight at once.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
                   const float2* __restrict__ ws_ml, const int4* __restrict__ ws_meta,
                   const int32_t* __restrict__ seq_lens, int32_t hkv, int32_t max_len) {
+  constexpr int kBatch = 4;
   const int pair = blockIdx.x;
   const int s = pair / hkv, kh = pair % hkv;
   const int64_t row0 = (int64_t)s * hkv * G + (int64_t)kh * G;
   const int L = seq_lens[s];
+  const int4 meta = ws_meta[pair];  // meaningful only when L is in range
   if (L <= 0 || L > max_len) {
     const float v = L == 0 ? 0.0f : __builtin_nanf("");
     for (int i = threadIdx.x; i < G * D; i += 256) out[row0 * D + i] = to_bits<T>(v);
     return;
   }
-  const int4 meta = ws_meta[pair];
   const int c_first = meta.x, c_last = meta.y;
   if (c_first == c_last) return;  // finished by one wave
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = threadIdx.x * 4; i < G * D; i += 256 * 4) {
     const int h = i / D, d = i % D;
-    float M = kNegInf;
-    for (int c = c_first; c <= c_last; ++c) {
-      const int64_t slot = 2 * (int64_t)c + (c == c_first ? meta.z : 0);
-      M = fmaxf(M, ws_ml[slot * G + h].x);
+    float M = kNegInf, den = 0.0f;
+    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = c_first; c0 <= c_last; c0 += kBatch) {
+      float2 ml[kBatch];
+      float4 a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + u;
+        ml[u] = make_float2(kNegInf, 0.0f);
+        a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c <= c_last) {
+          const int64_t slot = 2 * (int64_t)c + (c == c_first ? meta.z : 0);
+          ml[u] = ws_ml[slot * G + h];
+          a[u] = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
+      const float base = (Mb == kNegInf) ? 0.0f : Mb;
+      const float r = exp2_fast(M - base);  // rescale what is summed so far
+      den *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] *= r;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float f = exp2_fast(ml[u].x - base);
+        den = fmaf(f, ml[u].y, den);
+        num[0] = fmaf(f, a[u].x, num[0]);
+        num[1] = fmaf(f, a[u].y, num[1]);
+        num[2] = fmaf(f, a[u].z, num[2]);
+        num[3] = fmaf(f, a[u].w, num[3]);
+      }
+      M = Mb;
     }
-    const float base = (M == kNegInf) ? 0.0f : M;
-    float num = 0.0f, den = 0.0f;
-    for (int c = c_first; c <= c_last; ++c) {
-      const int64_t slot = 2 * (int64_t)c + (c == c_first ? meta.z : 0);
-      const float2 ml = ws_ml[slot * G + h];
-      const float f = exp2_fast(ml.x - base);
-      num = fmaf(f, ws_acc[(slot * G + h) * D + d], num);
-      den = fmaf(f, ml.y, den);
-    }
-    out[(row0 + h) * D + d] = to_bits<T>(num / den);
+    const uint2 o = make_uint2(pack2<T>(num[0] / den, num[1] / den),
+                               pack2<T>(num[2] / den, num[3] / den));
+    *reinterpret_cast<uint2*>(out + (row0 + h) * D + d) = o;
   }
 }
 
