@@ -19,6 +19,11 @@ Prints one JSON line:
               pa_probe_gather, which issues exactly pa_decode's K/V loads and
               computes nothing (the gather pattern's own ceiling)
   cpu_baseline  the float64 CPU oracle on the same step, host cores
+  host_block_manager  the host bookkeeping of the same step through the
+              block manager (include/pa_block_manager.h): one appended
+              token for each of the 256 sequences (pa_bm_append_batch) and
+              the 256 block tables pa_decode takes (pa_bm_tables), median
+              microseconds per step on the host
 """
 import argparse
 import json
@@ -83,6 +88,8 @@ def parse():
                     help="0: pa_decode's balanced split (stream-K); else explicit partitions")
     ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
                     help="pa_decode (matrix-core kernel) or pa_decode_valu")
+    ap.add_argument("--block-manager", choices=["on", "off"], default="on",
+                    help="time the host block manager's bookkeeping for the same step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (a transfer of "
                          "known size to scale HBM byte counters by)")
@@ -112,6 +119,35 @@ def cpu_baseline(b, seconds):
                    f"{t:.2f} s"),
         "seqs_per_s": round(b.num_seqs / t, 2),
     }
+
+
+def host_block_manager(b, steps=200):
+    """Median host time of one decode step's bookkeeping for the bench batch:
+    the manager holds the batch's sequences (random token ids, no shared
+    prefixes), then each step appends one token to every sequence and fills
+    the block tables and lengths pa_decode takes."""
+    import numpy as np
+    import paged_kv_cache_400_amd as pa
+    bs, S = b.block_size, b.num_seqs
+    lens = b.seq_lens.astype(np.int64)
+    mb = int((lens.max() + steps) // bs + 2)
+    nb = int(sum(-(-int(L) // bs) for L in lens)) + S * (steps // bs + 2)
+    bm = pa.BlockManager(nb, bs)
+    rng = np.random.default_rng(0)
+    for s in range(S):
+        bm.add_sequence(s, rng.integers(0, 1 << 15, int(lens[s])))
+    ids = np.arange(S, dtype=np.int64)
+    toks = rng.integers(0, 1 << 15, (steps, S)).astype(np.int32)
+    out = (np.empty((S, mb), np.int32), np.empty(S, np.int32))
+    times = []
+    for i in range(steps):
+        t0 = time.perf_counter()
+        bm.append_batch(ids, toks[i])
+        bm.tables(ids, mb, out=out)
+        times.append(time.perf_counter() - t0)
+    bm.close()
+    return {"us_per_step": round(float(np.median(times)) * 1e6, 1), "seqs": S, "steps": steps,
+            "ops": "append_batch (one token per sequence) + tables, through the Python binding"}
 
 
 def main():
@@ -250,6 +286,10 @@ def main():
                                    "gbs_read_plus_write": round(2 * n / (c0.elapsed_time(c1)
                                                                          * 1e-3) / 1e9, 1)}
         del src, dst
+    if args.block_manager == "on":
+        res["host_block_manager"] = host_block_manager(b)
+        res["host_block_manager"]["frac_of_step"] = round(
+            res["host_block_manager"]["us_per_step"] * 1e-3 / res["ms_per_step"], 4)
     if args.cpu_baseline == "on":
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -66,7 +66,9 @@ typedef enum pa_status {
   PA_ERR_SHAPE = 2,        /* inconsistent sizes, or a misaligned pointer      */
   PA_ERR_UNSUPPORTED = 3,  /* dtype, head_dim, block_size or group not built   */
   PA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required       */
-  PA_ERR_HIP = 5           /* the HIP runtime refused a launch                 */
+  PA_ERR_HIP = 5,          /* the HIP runtime refused a launch                 */
+  PA_ERR_NO_BLOCKS = 6     /* the block manager's pool cannot supply the blocks
+                              an operation needs (pa_block_manager.h)          */
 } pa_status;
 
 typedef enum pa_dtype {

@@ -7,7 +7,8 @@ package does not load the library; the first use of ``decode``,
 and fails loudly if it has not been built.
 """
 _BINDING_NAMES = ("decode", "reshape_and_cache", "copy_blocks", "decode_workspace_bytes",
-                  "probe_gather", "PaError", "abi_version", "LIB_PATH")
+                  "probe_gather", "BlockManager", "NoBlocks", "PaError", "abi_version",
+                  "LIB_PATH")
 
 
 def __getattr__(name):

@@ -15,11 +15,13 @@ import torch  # first: libpa binds to the HIP runtime torch has loaded
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
+(PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
+ PA_ERR_NO_BLOCKS) = range(7)
 PA_F16, PA_BF16 = 0, 1
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
-# (name, restype, argtypes) for every entry point of include/pa.h and include/pa_probe.h
+# (name, restype, argtypes) for every entry point of include/pa.h, include/pa_probe.h and
+# include/pa_block_manager.h
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -33,6 +35,16 @@ SIGNATURES = {
                                       ctypes.c_int, _vp]),
     "pa_probe_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, ctypes.c_int, _vp]),
+    "pa_bm_create": (ctypes.c_int, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_num_free": (_i32, [_vp]),
+    "pa_bm_add_sequence": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _i32, _vp, _vp]),
+    "pa_bm_append": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "pa_bm_append_batch": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "pa_bm_fork": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64]),
+    "pa_bm_free": (ctypes.c_int, [_vp, ctypes.c_int64]),
+    "pa_bm_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "pa_bm_block_refs": (_i32, [_vp, _i32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (ctypes.c_int32, []),
@@ -201,3 +213,126 @@ def probe_gather(k_cache, v_cache, block_tables, seq_lens, num_q_heads, sink=Non
                                 _ptr(seq_lens), S, num_q_heads, Hkv, d, bs, MB, NB,
                                 _DT[k_cache.dtype], _stream(dev)))
     return sink
+
+
+class NoBlocks(PaError):
+    """The block manager's pool cannot supply the blocks an operation needs."""
+
+
+def _bm_check(status: int):
+    if status == PA_ERR_NO_BLOCKS:
+        raise NoBlocks(status, "the pool has too few free blocks")
+    _check(status)
+
+
+def _i32_array(values):
+    """(contiguous int32 copy or view, its address).  The address goes to the
+    c_void_p argument as a plain integer: numpy's ctypes.data_as costs tens
+    of microseconds a call, more than the manager's own work."""
+    import numpy as np
+    a = np.ascontiguousarray(values, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+class BlockManager:
+    """Host-side block manager (include/pa_block_manager.h): free queue,
+    reference counts, block tables, copy-on-write and prefix cache.  Numpy
+    int32 arrays in and out; no device memory is touched."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        import numpy as np
+        self._np = np
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        order = None
+        if free_order is not None:
+            order, ptr = _i32_array(free_order)
+        else:
+            ptr = None
+        h = ctypes.c_void_p()
+        _check(_lib.pa_bm_create(self.num_blocks, self.block_size, ptr, ctypes.byref(h)))
+        self._h = h
+        del order
+
+    def close(self):
+        if self._h:
+            _lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(_lib.pa_bm_num_free(self._h))
+
+    def add_sequence(self, seq_id, tokens):
+        """Returns (number of leading tokens found cached, slots int32[n])."""
+        np = self._np
+        toks, tp = _i32_array(tokens)
+        slots = np.empty(len(toks), np.int32)
+        nc = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_add_sequence(self._h, int(seq_id), tp, len(toks),
+                                          slots.ctypes.data,
+                                          ctypes.byref(nc)))
+        return int(nc.value), slots
+
+    def append(self, seq_id, tokens):
+        """Returns (slots int32[n], copy-on-write pairs int32[k][2])."""
+        np = self._np
+        toks, tp = _i32_array(tokens)
+        slots = np.empty(len(toks), np.int32)
+        pairs = np.empty((1, 2), np.int32)
+        nc = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_append(self._h, int(seq_id), tp, len(toks),
+                                    slots.ctypes.data,
+                                    pairs.ctypes.data, 1, ctypes.byref(nc)))
+        return slots, pairs[:nc.value].copy()
+
+    def append_batch(self, seq_ids, tokens):
+        """One token per sequence (a decode step) in one call: returns (slots
+        int32[S], copy-on-write pairs int32[k][2]); all or nothing."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        toks, tp = _i32_array(tokens)
+        if toks.shape != ids.shape:
+            raise ValueError("one token per sequence")
+        slots = np.empty(len(ids), np.int32)
+        pairs = np.empty((max(1, len(ids)), 2), np.int32)
+        nc = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_append_batch(self._h, ids.ctypes.data, tp,
+                                          len(ids), slots.ctypes.data,
+                                          pairs.ctypes.data, len(pairs),
+                                          ctypes.byref(nc)))
+        return slots, pairs[:nc.value].copy()
+
+    def fork(self, parent_id, child_id):
+        _bm_check(_lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))
+
+    def free(self, seq_id):
+        _bm_check(_lib.pa_bm_free(self._h, int(seq_id)))
+
+    def tables(self, seq_ids, max_blocks_per_seq, pad_block=0, out=None):
+        """(block tables int32[S][max_blocks_per_seq], lengths int32[S]).
+        ``out``: a (tables, lengths) pair of C-contiguous int32 arrays of those
+        shapes to fill instead of new ones (pinned host tensors' numpy views
+        serve, for an asynchronous copy to the device)."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        if out is None:
+            t = np.empty((len(ids), max_blocks_per_seq), np.int32)
+            lens = np.empty(len(ids), np.int32)
+        else:
+            t, lens = out
+            for a, shape in ((t, (len(ids), max_blocks_per_seq)), (lens, (len(ids),))):
+                if a.dtype != np.int32 or a.shape != shape or not a.flags["C_CONTIGUOUS"]:
+                    raise ValueError(f"out arrays must be C-contiguous int32 of shape {shape}")
+        _bm_check(_lib.pa_bm_tables(self._h, ids.ctypes.data, len(ids),
+                                    int(max_blocks_per_seq), int(pad_block),
+                                    t.ctypes.data,
+                                    lens.ctypes.data))
+        return t, lens
+
+    def block_refs(self, block) -> int:
+        return int(_lib.pa_bm_block_refs(self._h, int(block)))

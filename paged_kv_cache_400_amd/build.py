@@ -1,6 +1,8 @@
-"""Build libpa.so (the HIP kernels and the C ABI of include/pa.h) for gfx950.
+"""Build libpa.so (the HIP kernels and the C ABI of include/pa.h, and the
+host-side block manager of include/pa_block_manager.h) for gfx950.
 
-Each ``csrc/*.hip`` file is compiled by hipcc in parallel, then linked into
+Each ``csrc/*.hip`` file is compiled by hipcc and each host-only
+``csrc/*.cpp`` file by the host C++ compiler, in parallel, then linked into
 ``paged_kv_cache_400_amd/libpa.so`` next to this file.  Packed-FP32 VALU
 instructions are disabled for all device code.
 """
@@ -28,13 +30,22 @@ CFLAGS = [
 ]
 
 
+HOST_CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", "/opt/rocm/include",
+              "-D__HIP_PLATFORM_AMD__"]
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """HIP sources (device + host code, hipcc) and host-only C++ sources (g++)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", obj], check=True)
+    if src.endswith(".cpp"):
+        subprocess.run([HOST_CXX, *HOST_FLAGS, "-c", src, "-o", obj], check=True)
+    else:
+        subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", obj], check=True)
     return obj
 
 

@@ -71,6 +71,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
   }
   return "PA_ERR_UNKNOWN";
 }

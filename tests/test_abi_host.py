@@ -14,7 +14,8 @@ import torch  # noqa: F401  (loads torch's HIP runtime first, as the binding doe
 from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "pa.h")
-HEADERS = [HEADER, os.path.join(ROOT, "include", "pa_probe.h")]
+HEADERS = [HEADER, os.path.join(ROOT, "include", "pa_probe.h"),
+           os.path.join(ROOT, "include", "pa_block_manager.h")]
 LIB = os.path.join(ROOT, "paged_kv_cache_400_amd", "libpa.so")
 
 
