@@ -9,7 +9,10 @@ sides use; it holds none of the method's arithmetic.
 What is here:
   * ``pa_oracle.c`` (built by ``build.py``): fp64 paged decode attention, its
     split-by-partition form merged by log-sum-exp, the append
-    (reshape_and_cache), the copy-on-write block copy and the slot formula.
+    (reshape_and_cache), the copy-on-write block copy and the slot formula;
+    for 8-bit pools (OCP E4M3, one scale per pool) the code <-> value maps,
+    the quantising append and decode over the dequantised pools.
+  * ``block_manager``: a plain-Python model of the host block manager.
   * ``accounting``: block counts and KV byte arithmetic of the worked memory
     example ("What problem does PagedAttention solve ...", section "A
     concrete memory example").
@@ -55,8 +58,18 @@ def lib():
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_double.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_double.restype = ctypes.c_double
+        L.oracle_e4m3_from_float.argtypes = [f32]
+        L.oracle_e4m3_from_float.restype = ctypes.c_uint8
+        L.oracle_quantize_e4m3.argtypes = [vp, vp, ctypes.c_int64, i32, f32]
+        L.oracle_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                   f32, f32, i32]
+        L.oracle_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, f32, f32, f32, i32, vp, i32]
         for name in ("oracle_decode", "oracle_decode_split", "oracle_reshape_and_cache",
-                     "oracle_copy_blocks", "oracle_slot_mapping"):
+                     "oracle_copy_blocks", "oracle_slot_mapping", "oracle_quantize_e4m3",
+                     "oracle_reshape_and_cache_fp8", "oracle_decode_fp8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,4 +187,82 @@ def slot_mapping(block_tables, seq_ids, positions, block_size):
     out = np.zeros(si.shape, dtype=np.int32)
     _check(lib().oracle_slot_mapping(_p(out), _p(bt), _p(si), _p(pos), si.shape[0], bt.shape[1],
                                      int(block_size)))
+    return out
+
+
+# ---- 8-bit (OCP E4M3) KV pools
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError(f"expected E4M3 codes (uint8), got {a.dtype}")
+    return a
+
+
+def e4m3_to_double(codes):
+    """Exact value of each E4M3 code as float64 (NaN for the NaN codes)."""
+    flat = np.asarray(codes, dtype=np.uint8).ravel()
+    f = lib().oracle_e4m3_to_double
+    return np.array([f(int(c)) for c in flat], dtype=np.float64).reshape(np.shape(codes))
+
+
+def e4m3_from_float(y):
+    """Nearest E4M3 code (ties to even, saturating) of each float32 value."""
+    flat = np.asarray(y, dtype=np.float32).ravel()
+    f = lib().oracle_e4m3_from_float
+    return np.array([f(float(v)) for v in flat], dtype=np.uint8).reshape(np.shape(y))
+
+
+def quantize_e4m3(bits, dtype, scale):
+    """Codes of x / scale for raw 16-bit patterns x of ``dtype``."""
+    x = _u16(bits)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _check(lib().oracle_quantize_e4m3(_p(out), _p(x), x.size, dtype, float(np.float32(scale))))
+    return out
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale, dtype):
+    """Quantising append in place on host copies of 8-bit pools."""
+    key, value = _u16(key), _u16(value)
+    for a in (k_cache, v_cache):
+        if a.dtype != np.uint8 or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("pools must be contiguous uint8")
+    sm = _i32(slot_mapping)
+    T, Hkv, d = key.shape
+    NB, Hkv2, bs, d2 = k_cache.shape
+    assert Hkv2 == Hkv and d2 == d and sm.shape == (T,) and v_cache.shape == k_cache.shape
+    _check(lib().oracle_reshape_and_cache_fp8(_p(key), _p(value), _p(k_cache), _p(v_cache),
+                                              _p(sm), T, Hkv, d, bs, NB,
+                                              float(np.float32(k_scale)),
+                                              float(np.float32(v_scale)), dtype))
+
+
+def copy_blocks_fp8(k_cache, v_cache, block_mapping):
+    """Copy-on-write block copies of 8-bit pools: the same byte copy as
+    ``copy_blocks``, run on the pools' bytes two at a time."""
+    for a in (k_cache, v_cache):
+        if a.dtype != np.uint8 or not a.flags["C_CONTIGUOUS"] or a.shape[-1] % 2:
+            raise ValueError("pools must be contiguous uint8 with an even head_dim")
+    copy_blocks(k_cache.view(np.uint16), v_cache.view(np.uint16), block_mapping)
+
+
+def decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, dtype,
+               pairs=None):
+    """fp64 paged decode attention over 8-bit pools (codes read as
+    e4m3(code) * scale of the pool); otherwise as ``decode``."""
+    q, k_cache, v_cache = _u16(q), _u8(k_cache), _u8(v_cache)
+    bt, sl = _i32(block_tables), _i32(seq_lens)
+    S, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    assert d2 == d and v_cache.shape == k_cache.shape and bt.shape[0] == S and sl.shape == (S,)
+    out = np.full((S, Hq, d), np.nan, dtype=np.float64)
+    if pairs is not None:
+        pr = _i32(np.asarray(pairs).reshape(-1, 2))
+        pp, npairs = _p(pr), pr.shape[0]
+    else:
+        pr, pp, npairs = None, None, 0
+    _check(lib().oracle_decode_fp8(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(bt), _p(sl), S,
+                                   Hq, Hkv, d, bs, bt.shape[1], NB, float(np.float32(scale)),
+                                   float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                   dtype, pp, npairs))
     return out

@@ -407,3 +407,195 @@ int oracle_copy_blocks(uint16_t* k_cache, uint16_t* v_cache,
   free(snap);
   return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * 8-bit KV cache (OCP FP8 E4M3, one scale per pool).
+ *
+ * The pages name quantising the KV cache as a way to cut the bytes each
+ * token costs ("What problem does PagedAttention solve, and what is
+ * continuous batching?", sections "Why the KV cache becomes the problem" and
+ * "What they'll ask next"), and fix neither the format nor the scaling.
+ * Readings taken:
+ *  - element format: OCP 8-bit floating point, E4M3 (the "fn" variant: no
+ *    infinities, S.1111.111 is NaN, largest finite 448);
+ *  - one float32 scale per pool: the stored code c stands for
+ *    e4m3(c) * k_scale (keys) or e4m3(c) * v_scale (values);
+ *  - quantising: y = x / scale rounded once to float32, then to the nearest
+ *    E4M3 value, ties to the even code, saturating: |y| >= 448 (infinities
+ *    included) gives +-448; NaN gives the NaN code with y's sign.
+ * ------------------------------------------------------------------------ */
+
+/* E4M3: sign, 4-bit exponent (bias 7), 3-bit fraction.
+ * Normal:    (-1)^s * (8 + f) * 2^(e - 10)       (e = 1..15, not e=15,f=7)
+ * Subnormal: (-1)^s * f * 2^-9                   (e = 0)
+ * e = 15, f = 7: NaN.                                                       */
+double oracle_e4m3_to_double(uint8_t c) {
+  int s = (c >> 7) & 1;
+  int e = (c >> 3) & 0xf;
+  int f = c & 0x7;
+  double v;
+  if (e == 15 && f == 7)
+    return NAN;
+  if (e == 0)
+    v = ldexp((double)f, -9);
+  else
+    v = ldexp((double)(8 + f), e - 10);
+  return s ? -v : v;
+}
+
+/* Nearest E4M3 code to the float32 value y: every finite magnitude code
+ * 0x00..0x7E is tried, the closest wins, and of two equally close the even
+ * code (even last fraction bit) wins.  Saturating; NaN -> NaN code. */
+uint8_t oracle_e4m3_from_float(float y) {
+  uint32_t bits;
+  memcpy(&bits, &y, sizeof bits);
+  const uint8_t sign = (uint8_t)((bits >> 31) << 7);
+  if (y != y) return (uint8_t)(sign | 0x7f);
+  const double a = fabs((double)y);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7e);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7e; ++c) {
+    const double err = fabs(oracle_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* The float32 quotient x / scale: the exact quotient of two float32 values
+ * rounded to double and then to float32 is the correctly rounded float32
+ * quotient (53 >= 2 * 24 + 2, so the double rounding is innocuous). */
+static float quotient_f32(double x, float scale) { return (float)(x / (double)scale); }
+
+/* codes[i] = E4M3 code of x[i] / scale, x raw 16-bit patterns of dtype. */
+int oracle_quantize_e4m3(uint8_t* codes, const uint16_t* x, int64_t n, int32_t dtype,
+                         float scale) {
+  if (n < 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) || !(scale > 0.0f) ||
+      scale == INFINITY)
+    return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    codes[i] = oracle_e4m3_from_float(quotient_f32(widen(x[i], dtype), scale));
+  return ORACLE_OK;
+}
+
+/*
+ * Append into 8-bit pools: for every token i with slot_mapping[i] >= 0 and
+ * every KV head h, k_cache[slot / bs][h][slot % bs][j] = code of
+ * key[i][h][j] / k_scale (values with v_scale).  Same slot rules as
+ * oracle_reshape_and_cache.
+ */
+int oracle_reshape_and_cache_fp8(const uint16_t* key, const uint16_t* value, uint8_t* k_cache,
+                                 uint8_t* v_cache, const int32_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, float k_scale,
+                                 float v_scale, int32_t dtype) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+      !(k_scale > 0.0f) || !(v_scale > 0.0f) || k_scale == INFINITY || v_scale == INFINITY)
+    return ORACLE_BAD_ARG;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    if (slot_mapping[i] >= num_slots) return ORACLE_BAD_SLOT;
+    for (int32_t j = 0; j < i; ++j)
+      if (slot_mapping[i] >= 0 && slot_mapping[j] == slot_mapping[i]) return ORACLE_DUP_SLOT;
+  }
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    int64_t b = slot / block_size, o = slot % block_size;
+    for (int32_t h = 0; h < num_kv_heads; ++h) {
+      int64_t src = ((int64_t)i * num_kv_heads + h) * head_dim;
+      int64_t dst = ((b * num_kv_heads + h) * block_size + o) * head_dim;
+      for (int32_t j = 0; j < head_dim; ++j) {
+        k_cache[dst + j] = oracle_e4m3_from_float(quotient_f32(widen(key[src + j], dtype), k_scale));
+        v_cache[dst + j] =
+            oracle_e4m3_from_float(quotient_f32(widen(value[src + j], dtype), v_scale));
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Decode attention over 8-bit pools: exactly oracle_decode with every stored
+ * key element read as e4m3(code) * k_scale and every value element as
+ * e4m3(code) * v_scale (both products exact in double).  q and out as in
+ * oracle_decode.
+ */
+int oracle_decode_fp8(double* out, const uint16_t* q, const uint8_t* k_cache,
+                      const uint8_t* v_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                      float k_scale, float v_scale, int32_t dtype, const int32_t* pairs,
+                      int32_t num_pairs) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      num_q_heads % num_kv_heads != 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+    return ORACLE_BAD_ARG;
+  int rc = check_tables(block_tables, seq_lens, num_seqs, max_blocks_per_seq,
+                        block_size, num_blocks);
+  if (rc != ORACLE_OK) return rc;
+  const int64_t n = pairs ? (int64_t)num_pairs : (int64_t)num_seqs * num_q_heads;
+  for (int64_t k = 0; pairs && k < n; ++k)
+    if (pairs[2 * k] < 0 || pairs[2 * k] >= num_seqs || pairs[2 * k + 1] < 0 ||
+        pairs[2 * k + 1] >= num_q_heads)
+      return ORACLE_BAD_ARG;
+  int32_t max_len = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) max_len = seq_lens[s] > max_len ? seq_lens[s] : max_len;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const double ks = (double)k_scale, vs = (double)v_scale, sc = (double)scale;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    if (!z || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t k = 0; k < n; ++k) {
+        int32_t s = pairs ? pairs[2 * k] : (int32_t)(k / num_q_heads);
+        int32_t h = pairs ? pairs[2 * k + 1] : (int32_t)(k % num_q_heads);
+        int32_t kh = h / group;
+        double* o = out + ((int64_t)s * num_q_heads + h) * head_dim;
+        const uint16_t* qv = q + ((int64_t)s * num_q_heads + h) * head_dim;
+        int32_t L = seq_lens[s];
+        if (L == 0) {
+          for (int32_t i = 0; i < head_dim; ++i) o[i] = 0.0;
+          continue;
+        }
+        for (int32_t t = 0; t < L; ++t) {
+          int64_t slot = slot_of(block_tables, max_blocks_per_seq, block_size, s, t);
+          int64_t b = slot / block_size, off = slot % block_size;
+          const uint8_t* kt = k_cache + ((b * num_kv_heads + kh) * block_size + off) * head_dim;
+          double dot = 0.0;
+          for (int32_t i = 0; i < head_dim; ++i)
+            dot += widen(qv[i], dtype) * (oracle_e4m3_to_double(kt[i]) * ks);
+          z[t] = sc * dot;
+        }
+        double m = -INFINITY;
+        for (int32_t t = 0; t < L; ++t) m = z[t] > m ? z[t] : m;
+        double l = 0.0;
+        for (int32_t i = 0; i < head_dim; ++i) acc[i] = 0.0;
+        for (int32_t t = 0; t < L; ++t) {
+          double w = exp(z[t] - m);
+          l += w;
+          int64_t slot = slot_of(block_tables, max_blocks_per_seq, block_size, s, t);
+          int64_t b = slot / block_size, off = slot % block_size;
+          const uint8_t* vt = v_cache + ((b * num_kv_heads + kh) * block_size + off) * head_dim;
+          for (int32_t i = 0; i < head_dim; ++i) acc[i] += w * (oracle_e4m3_to_double(vt[i]) * vs);
+        }
+        for (int32_t i = 0; i < head_dim; ++i) o[i] = acc[i] / l;
+      }
+    }
+    free(z);
+    free(acc);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}

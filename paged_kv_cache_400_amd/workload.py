@@ -23,11 +23,21 @@ them:
   * ``[seed, 3, s]``   sequence s's K rows then V rows for every position it
                        holds after the step ([n][Hkv][d] each);
   * ``[seed, 4]``      a shared prefix's K rows then V rows;
-  * ``[seed, 5]``      padding rows of the append and their shuffle.
+  * ``[seed, 5]``      padding rows of the append and their shuffle;
+  * ``[seed, 6, s]``   8-bit pools: sequence s's K codes then V codes for
+                       the positions already in the pool;
+  * ``[seed, 7, s]``   8-bit pools: its 16-bit K rows then V rows for the
+                       positions the step appends.
 Values are float32 standard normal rounded to fp16/bf16 by
 round-to-nearest-even.
 Pool slots that hold no token are NaN (0x7E00 fp16, 0x7FC0 bf16); table
 entries past a sequence's last block point at a never-allocated NaN block.
+
+8-bit pools (``kv="fp8"``) hold OCP E4M3 codes drawn directly, not made from
+values (no quantising happens here): a uniform sign bit and a magnitude code
+uniform in 0x00..0x77 (0 to 240), i.e. values up to 3.75 at the default
+scale 2^-6; slots that hold no token hold the NaN code 0x7F.  The appended
+tokens' rows stay 16-bit N(0, 1) values, which the step's append quantises.
 """
 import math
 import os
@@ -71,6 +81,9 @@ class PagedBatch:
     block_mapping: np.ndarray        # int32 [n][2] (src, dst)
     poison_block: int                # a NaN block no sequence owns
     info: Dict = field(default_factory=dict)
+    kv: str = "16"                   # "16": pools of `dtype`; "fp8": E4M3 codes (uint8)
+    k_scale: float = 1.0             # 8-bit pools: value of a key code = e4m3(code) * k_scale
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -82,7 +95,7 @@ class PagedBatch:
 
     @property
     def elem_bytes(self) -> int:
-        return 2
+        return 1 if self.kv == "fp8" else 2
 
     def kv_bytes(self, lens=None) -> int:
         """Live K+V bytes one decode reads: sum_s L_s * 2 * Hkv * d * 2."""
@@ -129,13 +142,41 @@ def _seq_rows(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
     return k, v
 
 
-def _all_rows(seed: int, counts, hkv: int, d: int, dtype: str):
+def _all_rows(seed: int, counts, hkv: int, d: int, dtype: str, fn=None):
     """Rows of every sequence, drawn on a thread pool (numpy releases the GIL)."""
+    fn = _seq_rows if fn is None else fn
     workers = max(1, min(16, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
-        futs = [ex.submit(_seq_rows, seed, s, int(n), hkv, d, dtype)
+        futs = [ex.submit(fn, seed, s, int(n), hkv, d, dtype)
                 for s, n in enumerate(counts)]
         return [f.result() for f in futs]
+
+
+FP8_NAN = 0x7F
+FP8_MAX_MAG_CODE = 0x77
+FP8_DEFAULT_SCALE = 2.0 ** -6
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> torch.Tensor:
+    """Random E4M3 codes: uniform sign, magnitude code uniform in
+    [0, FP8_MAX_MAG_CODE]."""
+    mag = rng.integers(0, FP8_MAX_MAG_CODE + 1, size=shape, dtype=np.uint8)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    return torch.from_numpy(mag | sign)
+
+
+def _seq_codes(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
+    """Sequence s's K and V codes for n stored positions, stream [seed, 6, s]."""
+    rng = np.random.default_rng([seed, 6, s])
+    return fp8_codes(rng, (n, hkv, d)), fp8_codes(rng, (n, hkv, d))
+
+
+def _seq_new_rows(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
+    """16-bit K and V rows of the n tokens sequence s appends, stream [seed, 7, s]."""
+    rng = np.random.default_rng([seed, 7, s])
+    k = _round(rng.standard_normal((n, hkv, d), dtype=np.float32), dtype)
+    v = _round(rng.standard_normal((n, hkv, d), dtype=np.float32), dtype)
+    return k, v
 
 
 class _FreeList:
@@ -166,7 +207,9 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
                       head_dim: int, block_size: int, dtype: str, seed: int,
                       append: int = 1, num_blocks: Optional[int] = None,
                       pool_slack: float = 0.10, scale: Optional[float] = None,
-                      pad_tokens: int = 0, placement_seed: Optional[int] = None) -> PagedBatch:
+                      pad_tokens: int = 0, placement_seed: Optional[int] = None,
+                      kv: str = "16", k_scale: float = FP8_DEFAULT_SCALE,
+                      v_scale: float = FP8_DEFAULT_SCALE) -> PagedBatch:
     """A batch of independent sequences (no sharing).
 
     ``context_lens[s]`` tokens are already in the pool; ``append`` (0 or 1)
@@ -175,7 +218,11 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     sequence order, then blocks attached by the append.  ``pad_tokens`` extra
     new-token rows with slot -1 are interleaved (the append skips them).
     ``placement_seed`` (default ``seed``) changes only where blocks go.
+    ``kv="fp8"``: 8-bit pools of E4M3 codes with scales k_scale / v_scale
+    (the 16-bit ``dtype`` is then that of q, the new rows and the output).
     """
+    if kv not in ("16", "fp8"):
+        raise ValueError(f"kv must be '16' or 'fp8', got {kv!r}")
     ctx = np.asarray(context_lens, dtype=np.int32)
     S = len(ctx)
     bs = block_size
@@ -203,20 +250,35 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     d, Hq, Hkv = head_dim, num_q_heads, num_kv_heads
     q = _round(np.random.default_rng([seed, 2]).standard_normal((S, Hq, d), dtype=np.float32),
                dtype)
-    k_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
-    v_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
     new_k, new_v, seqs, poss = [], [], [], []
-    rows = _all_rows(seed, lens, Hkv, d, dtype)
+    if kv == "fp8":
+        k_pool = torch.full((num_blocks, Hkv, bs, d), FP8_NAN, dtype=torch.uint8)
+        v_pool = torch.full((num_blocks, Hkv, bs, d), FP8_NAN, dtype=torch.uint8)
+        codes = _all_rows(seed, ctx, Hkv, d, dtype, _seq_codes)
+        fresh = _all_rows(seed, lens - ctx, Hkv, d, dtype, _seq_new_rows)
+    else:
+        k_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
+        v_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
+        rows = _all_rows(seed, lens, Hkv, d, dtype)
     for s in range(S):
         L = int(lens[s])
-        K, V = rows[s]
-        rows[s] = None
         c = int(ctx[s])
-        _place(k_pool, owned[s], K[:c])
-        _place(v_pool, owned[s], V[:c])
+        if kv == "fp8":
+            K, V = codes[s]
+            codes[s] = None
+            _place(k_pool, owned[s], K)
+            _place(v_pool, owned[s], V)
+            K, V = fresh[s]
+            base = c
+        else:
+            K, V = rows[s]
+            rows[s] = None
+            _place(k_pool, owned[s], K[:c])
+            _place(v_pool, owned[s], V[:c])
+            base = 0
         for t in range(c, L):
-            new_k.append(K[t])
-            new_v.append(V[t])
+            new_k.append(K[t - base])
+            new_v.append(V[t - base])
             seqs.append(s)
             poss.append(t)
     T = len(seqs)
@@ -250,7 +312,9 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
                       seq_lens=lens.astype(np.int32), new_key=nk.contiguous(),
                       new_value=nv.contiguous(), slot_mapping=slot.astype(np.int32),
                       append_seq=seqs_a, append_pos=poss_a,
-                      block_mapping=np.zeros((0, 2), dtype=np.int32), poison_block=poison)
+                      block_mapping=np.zeros((0, 2), dtype=np.int32), poison_block=poison,
+                      kv=kv, k_scale=float(np.float32(k_scale)) if kv == "fp8" else 1.0,
+                      v_scale=float(np.float32(v_scale)) if kv == "fp8" else 1.0)
 
 
 # --------------------------------------------------------------------------
@@ -282,13 +346,15 @@ def mixed_lengths(num_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
 
 
 def make_mixed_step(seed: int = 3, num_seqs: int = 256, lo: int = 64, hi: int = 4096,
-                    dtype: str = "bf16") -> PagedBatch:
+                    dtype: str = "bf16", kv: str = "16") -> PagedBatch:
     """Continuous-batching decode step: 256 sequences with context lengths
     uniform in [64, 4096], 32 q / 8 KV heads, d 128, bf16, block 16, pool =
     total blocks + 10% from a seeded shuffled free list; the step appends one
-    token per sequence, then decodes over context + 1."""
+    token per sequence, then decodes over context + 1.  ``kv="fp8"``: the
+    same step over 8-bit pools."""
     ctx = mixed_lengths(num_seqs, lo, hi, seed)
-    b = make_decode_batch("mixed_step", ctx, 32, 8, 128, 16, dtype, seed, append=1)
+    b = make_decode_batch("mixed_step" if kv == "16" else "mixed_step_fp8", ctx, 32, 8, 128, 16,
+                          dtype, seed, append=1, kv=kv)
     return b
 
 

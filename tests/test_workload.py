@@ -93,3 +93,24 @@ def test_long_context_logical_data_do_not_depend_on_block_size(bs):
     a = wl.make_decode_batch("x", [40, 70], 8, 2, 16, bs, "bf16", seed=5, append=0)
     ref = wl.make_decode_batch("x", [40, 70], 8, 2, 16, 16, "bf16", seed=5, append=0)
     assert np.array_equal(bits(a.q), bits(ref.q))
+
+
+def test_fp8_pools_hold_drawn_codes_and_nan_elsewhere():
+    b = wl.make_decode_batch("fp8_gen", [50, 17, 16, 3], 8, 2, 64, 16, "bf16", 1, append=1,
+                             num_blocks=64, kv="fp8")
+    k, v = b.k_cache.numpy(), b.v_cache.numpy()
+    assert k.dtype == np.uint8 and b.elem_bytes == 1 and b.k_scale == 2.0 ** -6
+    live = np.zeros(k.shape[0] * 16, bool)
+    for s, c in enumerate(b.context_lens):
+        for p in range(int(c)):
+            live[b.block_tables[s, p // 16] * 16 + p % 16] = True
+    flat_k = k.transpose(0, 2, 1, 3).reshape(-1, 2 * 64)
+    flat_v = v.transpose(0, 2, 1, 3).reshape(-1, 2 * 64)
+    assert np.all((flat_k[live] & 0x7F) <= 0x77) and np.all((flat_v[live] & 0x7F) <= 0x77)
+    assert np.all(flat_k[~live] == 0x7F) and np.all(flat_v[~live] == 0x7F)
+    # both signs and the whole magnitude range appear
+    assert (flat_k[live] >> 7).min() == 0 and (flat_k[live] >> 7).max() == 1
+    assert (flat_k[live] & 0x7F).max() == 0x77 and (flat_k[live] & 0x7F).min() == 0
+    # the appended rows are 16-bit values, one per sequence
+    assert b.new_key.dtype == torch.bfloat16 and b.new_key.shape == (4, 2, 64)
+    assert b.kv_bytes() == int(b.seq_lens.sum()) * 2 * 2 * 64
