@@ -72,8 +72,11 @@ typedef enum pa_status {
 } pa_status;
 
 typedef enum pa_dtype {
-  PA_F16 = 0,   /* IEEE binary16 */
-  PA_BF16 = 1   /* bfloat16      */
+  PA_F16 = 0,       /* IEEE binary16                                          */
+  PA_BF16 = 1,      /* bfloat16                                               */
+  PA_FP8_E4M3 = 2   /* OCP 8-bit E4M3 ("fn": no infinities, 448 largest finite,
+                       S.1111.111 NaN); pool elements only (pa_copy_blocks,
+                       pa_probe_gather); see pa_decode_fp8                    */
 } pa_dtype;
 
 /*
@@ -165,6 +168,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
  * block src.  A src may appear in several pairs; dsts must be distinct and
  * no dst may be a src (then the result equals a copy from a snapshot taken
  * before the call).  Pairs with an id outside [0, num_blocks) are skipped.
+ * dtype is the pool element: PA_F16, PA_BF16 or PA_FP8_E4M3 (then head_dim
+ * must be a multiple of 16).
  *
  * Errors: as pa_reshape_and_cache.
  */
@@ -172,6 +177,50 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype dtype,
                          hipStream_t stream);
+
+/*
+ * 8-bit KV cache.  The pages name quantising the KV cache as a way to cut
+ * the bytes each token costs ("What problem does PagedAttention solve, and
+ * what is continuous batching?", sections "Why the KV cache becomes the
+ * problem" and "What they'll ask next") without fixing a format.  Here: the
+ * pools hold OCP E4M3 codes, one byte per element in the same
+ * [num_blocks][num_kv_heads][block_size][head_dim] layout, and each pool has
+ * one float32 scale: a key code c stands for e4m3(c) * k_scale, a value code
+ * for e4m3(c) * v_scale.
+ *
+ * pa_decode_fp8: pa_decode over 8-bit pools, always with the balanced split
+ * (tiles of 32 positions).  q and out are `dtype` (PA_F16 or PA_BF16); keys
+ * and values are widened exactly to `dtype` for the products; scores,
+ * softmax and sums are float32 as in pa_decode (the softmax weights rounded
+ * to `dtype` for the P.V product).  Workspace: pa_decode_workspace_bytes(
+ * num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, 0).  Same
+ * supported sizes, contract for unused slots and table entries, NaN rows for
+ * contract violations, and errors as pa_decode; k_scale and v_scale must be
+ * positive and finite (PA_ERR_SHAPE).
+ */
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        float scale, float k_scale, float v_scale, pa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Quantising append into 8-bit pools: for each token i with slot_mapping[i]
+ * >= 0 and each KV head h, k_cache[slot / bs][h][slot % bs][j] =
+ * E4M3(key[i][h][j] / k_scale) (values with v_scale), where the quotient is
+ * the correctly rounded float32 quotient and E4M3(y) is the nearest E4M3
+ * value, ties to the even code, saturating to +-448 (infinities included);
+ * NaN gives the NaN code with its sign.  key and value are `dtype` (PA_F16
+ * or PA_BF16).  Slot rules as pa_reshape_and_cache.  Errors as
+ * pa_reshape_and_cache, plus PA_ERR_UNSUPPORTED for head_dim not a multiple
+ * of 16 and PA_ERR_SHAPE for a scale that is not positive and finite.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                   void* v_cache, const int32_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, float k_scale,
+                                   float v_scale, pa_dtype dtype, hipStream_t stream);
 
 /* Static name of a status code. */
 const char* pa_status_string(pa_status status);

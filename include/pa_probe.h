@@ -25,7 +25,8 @@ extern "C" {
  * of pa_decode (the query and output arrays are replaced by `sink`).
  * `sink` is a caller-owned device buffer of at least 2 bytes; the call may
  * write it (only when the loaded data XOR to one particular word) and never
- * reads it.  Asynchronous on `stream`, like pa_decode.
+ * reads it.  Asynchronous on `stream`, like pa_decode.  dtype PA_FP8_E4M3
+ * selects 8-bit pools and reads exactly what pa_decode_fp8 reads.
  *
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_HIP.
  */

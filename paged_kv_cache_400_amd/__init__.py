@@ -2,13 +2,12 @@
 
 The compute lives in ``libpa.so`` (hand-written HIP kernels behind the C ABI
 of ``include/pa.h``); :mod:`.binding` is its Python binding.  Importing this
-package does not load the library; the first use of ``decode``,
-``reshape_and_cache``, ``copy_blocks`` or ``decode_workspace_bytes`` does,
+package does not load the library; the first use of one of its names does,
 and fails loudly if it has not been built.
 """
 _BINDING_NAMES = ("decode", "reshape_and_cache", "copy_blocks", "decode_workspace_bytes",
-                  "probe_gather", "BlockManager", "NoBlocks", "PaError", "abi_version",
-                  "LIB_PATH")
+                  "decode_fp8", "reshape_and_cache_fp8", "probe_gather", "BlockManager",
+                  "NoBlocks", "PaError", "abi_version", "LIB_PATH")
 
 
 def __getattr__(name):

@@ -17,8 +17,11 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
  PA_ERR_NO_BLOCKS) = range(7)
-PA_F16, PA_BF16 = 0, 1
+PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+# pool element types: 16-bit pools hold `dtype` values, 8-bit pools (uint8
+# tensors) hold OCP E4M3 codes
+_POOL_DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
 
 # (name, restype, argtypes) for every entry point of include/pa.h, include/pa_probe.h and
 # include/pa_block_manager.h
@@ -28,7 +31,12 @@ SIGNATURES = {
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _f32, _f32, _f32, ctypes.c_int, _vp, _sz,
+                                     _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                _i32, _f32, _f32, ctypes.c_int, _vp]),
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, ctypes.c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -158,6 +166,68 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_si
     return out
 
 
+def decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, k_scale, v_scale, scale=None,
+               out=None, workspace=None):
+    """pa_decode over 8-bit pools: k_cache/v_cache uint8 [NB][Hkv][bs][d] of
+    OCP E4M3 codes standing for e4m3(code) * k_scale (resp. v_scale); q and
+    out float16 or bfloat16.  Balanced split always."""
+    _need(q, "q", 3)
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    _need(k_cache, "k_cache", 4, torch.uint8, dev)
+    _need(v_cache, "v_cache", 4, torch.uint8, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("inconsistent shapes between q, the pools, block_tables and seq_lens")
+    MB = block_tables.shape[1]
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", 3, q.dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_bytes(S, Hq, d, MB, bs, 0)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None, None, dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB,
+                              float(scale), float(k_scale), float(v_scale), _DT[q.dtype],
+                              _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale):
+    """Quantising append: k_cache/v_cache (uint8 E4M3 codes)[slot // bs][:,
+    slot % bs] = E4M3(key/value[i] / scale) for slot >= 0."""
+    _need(key, "key", 3)
+    dev = key.device
+    if key.dtype not in _DT:
+        raise ValueError(f"key must be float16 or bfloat16, got {key.dtype}")
+    _need(value, "value", 3, key.dtype, dev)
+    _need(k_cache, "k_cache", 4, torch.uint8, dev)
+    _need(v_cache, "v_cache", 4, torch.uint8, dev)
+    _need(slot_mapping, "slot_mapping", 1, torch.int32, dev)
+    T, Hkv, d = key.shape
+    NB, Hkv2, bs, d2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or Hkv2 != Hkv or d2 != d or \
+            slot_mapping.shape[0] != T:
+        raise ValueError("inconsistent shapes between key/value, the pools and slot_mapping")
+    _check(_lib.pa_reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(slot_mapping), T, Hkv, d, bs, NB, float(k_scale),
+                                         float(v_scale), _DT[key.dtype], _stream(dev)))
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     """k_cache/v_cache[slot // bs][:, slot % bs] = key/value[i] for slot >= 0."""
     _need(key, "key", 3)
@@ -182,26 +252,28 @@ def copy_blocks(k_cache, v_cache, block_mapping):
     """For each (src, dst) row of block_mapping: block dst := block src (K and V)."""
     _need(k_cache, "k_cache", 4)
     dev = k_cache.device
-    if k_cache.dtype not in _DT:
-        raise ValueError(f"k_cache must be float16 or bfloat16, got {k_cache.dtype}")
+    if k_cache.dtype not in _POOL_DT:
+        raise ValueError(f"k_cache must be float16, bfloat16 or uint8 (E4M3 codes), got "
+                         f"{k_cache.dtype}")
     _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
     _need(block_mapping, "block_mapping", 2, torch.int32, dev)
     if v_cache.shape != k_cache.shape or block_mapping.shape[1] != 2:
         raise ValueError("pools must match and block_mapping must be [n][2]")
     NB, Hkv, bs, d = k_cache.shape
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
-                               block_mapping.shape[0], Hkv, d, bs, NB, _DT[k_cache.dtype],
+                               block_mapping.shape[0], Hkv, d, bs, NB, _POOL_DT[k_cache.dtype],
                                _stream(dev)))
 
 
 def probe_gather(k_cache, v_cache, block_tables, seq_lens, num_q_heads, sink=None):
     """Measurement support (include/pa_probe.h): read exactly the K/V bytes
     pa_decode's balanced split reads, with the same loads, computing nothing.
-    Returns the sink tensor (2 int16 words on the pools' device)."""
+    Returns the sink tensor (2 int16 words on the pools' device).  uint8
+    pools: what pa_decode_fp8 reads."""
     _need(k_cache, "k_cache", 4)
     dev = k_cache.device
-    if k_cache.dtype not in _DT:
-        raise ValueError(f"k_cache must be float16 or bfloat16, got {k_cache.dtype}")
+    if k_cache.dtype not in _POOL_DT:
+        raise ValueError(f"k_cache must be float16, bfloat16 or uint8, got {k_cache.dtype}")
     _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
     _need(block_tables, "block_tables", 2, torch.int32, dev)
     _need(seq_lens, "seq_lens", 1, torch.int32, dev)
@@ -211,7 +283,7 @@ def probe_gather(k_cache, v_cache, block_tables, seq_lens, num_q_heads, sink=Non
         sink = torch.zeros(2, dtype=torch.int16, device=dev)
     _check(_lib.pa_probe_gather(_ptr(sink), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                 _ptr(seq_lens), S, num_q_heads, Hkv, d, bs, MB, NB,
-                                _DT[k_cache.dtype], _stream(dev)))
+                                _POOL_DT[k_cache.dtype], _stream(dev)))
     return sink
 
 

@@ -1,6 +1,7 @@
 // cache_ops.hip -- the append (reshape_and_cache) and the copy-on-write block
 // copy (copy_blocks).  Both are pure data movement: 16-byte vector loads and
-// stores, one 16-byte chunk per thread, no arithmetic on the values.
+// stores, one 16-byte chunk per thread, no arithmetic on the values; and the
+// quantising append into 8-bit pools.
 //
 // Append: "Why the KV cache becomes the problem" (each decode step appends a
 // small amount of new data) and "Paged attention borrows a trick from
@@ -8,6 +9,7 @@
 // rows go to slot_mapping[i], i.e. block slot / bs, offset slot % bs.
 // Copy: "How PagedAttention works" (copy-on-write gives a diverging
 // candidate a private copy of a shared block).
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
@@ -31,6 +33,72 @@ pa_reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restri
   const int64_t dst = ((b * hkv + h) * bs + o) * chunks + c;
   k_cache[dst] = key[idx];
   v_cache[dst] = value[idx];
+}
+
+// ---- 8-bit pools ----------------------------------------------------------
+// Quantising append.  The pages name KV quantisation as the lever on bytes
+// per token ("What problem does PagedAttention solve, and what is continuous
+// batching?", sections "Why the KV cache becomes the problem" and "What
+// they'll ask next") and fix no format; this library stores OCP FP8 E4M3
+// codes with one float32 scale per pool: code = E4M3(x / scale), the
+// quotient rounded once to float32 (IEEE division), then to the nearest
+// E4M3 value with ties to the even code, saturating at +-448; NaN keeps its
+// sign and becomes the NaN code.
+
+// E4M3 code of y, from y's float32 bits (sign, 8-bit exponent, 23-bit
+// fraction) with the E4M3 grid: normal values (1 + f/8) 2^(e-7), e = 1..15,
+// and subnormals f 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;      // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;     // |y| >= 448 (inf included): saturate
+  if (a < 0x3c800000u) {                         // |y| < 2^-6: multiples of 2^-9
+    // |y| * 2^9 is exact; rounding it to an integer (ties to even) gives the
+    // code directly, 8 being the smallest normal 2^-6
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  // keep 3 of the 23 fraction bits, rounding to nearest even; a carry into
+  // the exponent is the correct next binade.  Code = (exponent - 120) << 3
+  // | fraction, as the float32 exponent bias is 127 and E4M3's is 7.
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+// One thread per (token, KV head, 16 elements): reads 32 bytes of key and of
+// value, writes 16 bytes of codes to each pool.
+template <typename T>
+__global__ void __launch_bounds__(256)
+pa_reshape_and_cache_fp8_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                                uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                const int32_t* __restrict__ slot_mapping, int64_t total,
+                                int32_t hkv, int32_t chunks, int32_t bs, int64_t num_slots,
+                                float k_scale, float v_scale) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int32_t c = (int32_t)(idx % chunks);
+  const int64_t th = idx / chunks;          // token * hkv + head
+  const int32_t h = (int32_t)(th % hkv);
+  const int64_t i = th / hkv;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
+  const int64_t b = slot / bs, o = slot % bs;
+  const int64_t dst = ((b * hkv + h) * bs + o) * chunks + c;
+  auto quantise16 = [&](const uint4* src, float scale) {
+    const uint4 x0 = src[2 * idx], x1 = src[2 * idx + 1];
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = w[2 * j], b2 = w[2 * j + 1];
+      q[j] = e4m3_code(lo_f32<T>(a) / scale) | (e4m3_code(hi_f32<T>(a) / scale) << 8) |
+             (e4m3_code(lo_f32<T>(b2) / scale) << 16) | (e4m3_code(hi_f32<T>(b2) / scale) << 24);
+    }
+    return make_uint4(q[0], q[1], q[2], q[3]);
+  };
+  k_cache[dst] = quantise16(key, k_scale);
+  v_cache[dst] = quantise16(value, v_scale);
 }
 
 // grid.x = pair; grid.y strides over the block's 16-byte chunks.
@@ -66,10 +134,28 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   return hipGetLastError();
 }
 
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                        void* v_cache, const int32_t* slot_mapping,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float k_scale, float v_scale, bool bf16,
+                                        hipStream_t stream) {
+  const int32_t chunks = head_dim / 16;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  const int64_t grid = (total + 255) / 256;
+  auto kernel = bf16 ? pa_reshape_and_cache_fp8_kernel<BF16> : pa_reshape_and_cache_fp8_kernel<F16>;
+  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(256), 0, stream, (const uint4*)key,
+                     (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, slot_mapping, total,
+                     num_kv_heads, chunks, block_size, (int64_t)num_blocks * block_size, k_scale,
+                     v_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                               int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int32_t num_blocks, hipStream_t stream) {
-  const int64_t block_chunks = (int64_t)num_kv_heads * block_size * head_dim / 8;
+                              int32_t block_size, int32_t num_blocks, int32_t elem_bytes,
+                              hipStream_t stream) {
+  const int64_t block_chunks = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes / 16;
   int64_t gy = (block_chunks + 255) / 256;
   if (gy > 64) gy = 64;
   hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3((uint32_t)num_pairs, (uint32_t)gy), dim3(256),

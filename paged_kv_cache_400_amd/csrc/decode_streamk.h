@@ -1,0 +1,450 @@
+// decode_streamk.h -- paged decode attention, the balanced (stream-K)
+// decomposition used by pa_decode when partition_size is 0 (and by
+// pa_decode_fp8), as templates: decode_streamk.hip instantiates them for
+// 16-bit pools, decode_fp8.hip for 8-bit E4M3 pools.
+//
+// What is computed is the same as the partitioned kernels: for every
+// sequence s and query head h, softmax attention of q[s][h] over positions
+// 0..L_s-1 read through the sequence's block table ("What problem does
+// PagedAttention solve ...", section "How PagedAttention works").  What
+// differs is how the work is cut.
+//
+// Global tile order: the (sequence, KV head) pairs back to back, pair
+// s * hkv + kh holding ceil(L_s / n) tiles of n positions (n = 16 for
+// 16-bit pools, 32 for 8-bit ones).  The launch has
+// exactly as many waves as the GPU keeps resident, and wave w takes the
+// contiguous run of tiles [w C, (w + 1) C) with C = ceil(total / waves)
+// (at least kMinChunk).  Every wave therefore streams the same number of
+// tiles (to one tile), never waits for another wave, and never sits idle at
+// the end of a work unit: the partitioned kernels spend a merge through LDS
+// and a barrier on every (sequence, head, 512-position) unit, and their
+// units differ in size.  Each wave finds its first pair from a prefix sum of
+// the tile counts (recomputed by every wave from seq_lens; a few hundred
+// integers from L2), then walks its run pair by pair:
+//   - a pair that lies wholly inside the run is finished in place: out =
+//     acc / l, rounded to the output type;
+//   - a pair cut by the run's start or end leaves a partial (m, l, acc) in
+//     the wave's slot 0 (the pair it starts in) or slot 1 (the pair it ends
+//     in) of the workspace;
+//   - the wave that processes a pair's last tile records which waves hold
+//     its partials (meta), and pa_streamk_reduce merges them by log-sum-exp
+//     ("Continuous Batching & Paged Attention", section "Attention needs
+//     memory that grows with the conversation": plain softmax attention; the
+//     merge is the identity M = max m_p, out = sum 2^(m_p - M) acc_p /
+//     sum 2^(m_p - M) l_p) and writes the zero rows of empty sequences and
+//     the NaN rows of sequences whose length breaks the contract.
+// Within a pair a wave consumes its tiles in order with TileWave
+// (pa_mfma.h) or TileWave8 (pa_mfma_fp8.h): K to registers, V to LDS, q.K^T
+// and P.V on MFMA, each tile issued one tile ahead.  The run's block ids are
+// staged in a register, one per lane, and read with v_readlane: no memory
+// access between two tiles.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_launch.h"
+#include "pa_mfma.h"
+#include "pa_mfma_fp8.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;              // waves per workgroup (independent)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMinChunk = 8;           // tiles per wave at least
+
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Lane i's value as a wave-uniform (scalar) value; i must be uniform.
+__device__ __forceinline__ int lane_value(int x, int i) {
+  return __builtin_amdgcn_readlane(x, i);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(x, m);
+    if (lane >= m) x += y;
+  }
+  return x;
+}
+
+}  // namespace
+
+// The tile wave of a pool element type: TileWave (pa_mfma.h) for 16-bit
+// pools, TileWave8 (pa_mfma_fp8.h) for 8-bit E4M3 pools.
+template <typename T, typename KV, int D, int BS, int G>
+struct TileWaveOf {
+  using type = TileWave<T, D, BS, G>;
+};
+template <typename T, int D, int BS, int G>
+struct TileWaveOf<T, FP8, D, BS, G> {
+  using type = TileWave8<T, D, BS, G>;
+};
+
+// kGather = true is the gather-only instantiation behind pa_probe_gather:
+// the same split, walk and K/V loads, no q, no arithmetic on the data and no
+// results (a word is written to `out` only if the XOR of the loaded data hits
+// a value it cannot be expected to hit).  KV is the pool element type (T, or
+// FP8 with out_scale = v_scale applied to every result; for 16-bit pools
+// out_scale is not used).
+template <typename T, int D, int BS, int G, bool kGather, typename KV>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
+                  float2* __restrict__ ws_ml, int4* __restrict__ ws_meta,
+                  const uint16_t* __restrict__ q,
+                  const typename TileWaveOf<T, KV, D, BS, G>::type::Elem* __restrict__ kc,
+                  const typename TileWaveOf<T, KV, D, BS, G>::type::Elem* __restrict__ vc,
+                  const int32_t* __restrict__ block_tables,
+                  const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t hkv,
+                  int32_t mb, int32_t nb, int32_t nwaves, float qk_scale, float out_scale) {
+  using TW = typename TileWaveOf<T, KV, D, BS, G>::type;
+  constexpr int KL = TW::KL, NM = TW::NM, kT = TW::kTileLen, kIds = TW::kIds;
+  constexpr bool kScaled = !std::is_same<KV, T>::value;
+  __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * TW::kTileBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = blockIdx.x * kWaves + w;
+  const int hq = hkv * G;
+  const int64_t max_len = (int64_t)mb * BS;
+  auto tiles_of = [&](int L) -> int {
+    return (L > 0 && (int64_t)L <= max_len) ? (L + kT - 1) / kT : 0;
+  };
+
+  // ---- this wave's run of the global tile order
+  int64_t per_head = 0;  // sum over sequences of their tile counts
+  for (int b = 0; b < num_seqs; b += 64) {
+    const int n = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) : 0;
+    per_head += wave_sum(n);
+  }
+  const int64_t total = per_head * hkv;
+  const int64_t chunk = max((int64_t)kMinChunk, (total + nwaves - 1) / nwaves);
+  const int64_t g0 = (int64_t)wave * chunk;
+  if (g0 >= total) return;
+  const int64_t g1 = min(total, g0 + chunk);
+
+  // first sequence whose tiles reach past g0, and where its pairs start
+  int s = -1;
+  int64_t seq_start = 0;  // global index of the sequence's first tile
+  {
+    int64_t run = 0;
+    for (int b = 0; b < num_seqs; b += 64) {
+      const int span = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) * hkv : 0;
+      const int incl = wave_inclusive_scan(span, lane);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(run + incl > g0);
+      if (hit != 0) {
+        const int i = __builtin_ctzll(hit);
+        s = b + i;
+        seq_start = run + lane_value(incl, i) - lane_value(span, i);
+        break;
+      }
+      run += lane_value(incl, 63);
+    }
+  }
+  if (s < 0) return;  // unreachable: g0 < total
+  int L = seq_lens[s];
+  int ns = tiles_of(L);
+  if (ns == 0) return;  // unreachable: the first hit has tiles
+  int kh = (int)((g0 - seq_start) / ns);
+  int t_lo = (int)((g0 - seq_start) % ns);
+
+  // The segment's result: final rows for a pair wholly inside the run, else
+  // a partial in slot 0 (the run's first pair) or 1 (its last); the wave
+  // holding a pair's last tile records where its partials are.  The G x D
+  // result leaves the MFMA layout 64 bytes per head row at a time, so it is
+  // staged row-major in the wave's V tiles (idle once the last tile is
+  // consumed) and stored 16 bytes per lane: whole, contiguous cache lines.
+  // (Stores of 32 or 64 bytes per instruction cost the mixed decode step 2%.)
+  auto write_result = [&](const TW& t, bool bad, int64_t row0, int t_lo,
+                          int t_hi, int ns, bool first, int64_t pair_start) {
+    const int col = lane & 15, grp = lane >> 4;
+    const bool whole = t_lo == 0 && t_hi == ns;
+    float* st = reinterpret_cast<float*>(t.vtile);  // [G][D]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * grp + r;
+      const float l_h = __shfl(t.l_run, h);
+      if (h < G) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          float v = whole ? t.acc[m][r] / l_h : t.acc[m][r];
+          if constexpr (kScaled) v *= out_scale;
+          st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : v;
+        }
+      }
+    }
+    // one wave's LDS accesses take effect in program order
+    if (whole) {
+      for (int i = lane * 8; i < G * D; i += 64 * 8) {
+        const float4 a = *reinterpret_cast<const float4*>(st + i);
+        const float4 b = *reinterpret_cast<const float4*>(st + i + 4);
+        *reinterpret_cast<uint4*>(out + row0 * D + i) =
+            make_uint4(pack2<T>(a.x, a.y), pack2<T>(a.z, a.w), pack2<T>(b.x, b.y),
+                       pack2<T>(b.z, b.w));
+      }
+    } else {
+      const int64_t slot = (int64_t)wave * 2 + (first ? 0 : 1);
+      for (int i = lane * 4; i < G * D; i += 64 * 4)
+        *reinterpret_cast<float4*>(ws_acc + slot * G * D + i) =
+            *reinterpret_cast<const float4*>(st + i);
+      if (lane < G)
+        ws_ml[slot * G + lane] = make_float2(t.m_run, bad ? __builtin_nanf("") : t.l_run);
+    }
+    if (t_hi == ns && lane == 0) {
+      const int c_first = (int)(pair_start / chunk);
+      const int c_last = (int)((pair_start + ns - 1) / chunk);
+      ws_meta[row0 / G] = make_int4(c_first, c_last, pair_start % chunk != 0, 0);
+    }
+  };
+  static_assert(sizeof(float) * G * D <= 2 * TW::kTileBytes, "the result fits the wave's V tiles");
+
+  TW tw;
+  unsigned char* vtile = s_mem + w * 2 * TW::kTileBytes;
+
+  int64_t g = g0;
+  while (true) {
+    // ---- one segment: pair (s, kh), tiles [t_lo, t_hi)
+    const int64_t pair_start = g - t_lo;  // global index of the pair's tile 0
+    const int t_hi = (int)min((int64_t)ns, (int64_t)t_lo + (g1 - g));
+    const int p_lo = t_lo * kT;
+    const int p_end = min(L, t_hi * kT);  // positions [p_lo, p_end)
+    const int ntiles = t_hi - t_lo;
+    const int64_t row0 = (int64_t)s * hq + (int64_t)kh * G;
+    const int32_t* bt_row = block_tables + (int64_t)s * mb;
+
+    tw.init(kc, vc, hkv, kh, vtile);
+    if constexpr (!kGather) tw.load_q(q + row0 * D);
+    tw.reset();
+    uint32_t gathered = 0;
+    auto consume = [&](const uint4 (&kr)[KL], int buf, int t0) {
+      if constexpr (kGather) {
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes);
+        gathered ^= kr[0].x ^ kr[KL - 1].w ^ vw[lane];
+      } else {
+        tw.consume(kr, buf, t0, p_end, qk_scale);
+      }
+    };
+
+    // block ids of the segment, 64 at a time: lane j holds block blk_base + j
+    const int blk_last = (p_end - 1) / BS;
+    int blk_base = p_lo / BS;
+    bool bad = false;
+    auto load_ids = [&]() {
+      int id = 0;
+      if (blk_base + lane <= blk_last) {
+        id = bt_row[blk_base + lane];
+        if (id < 0 || id >= nb) {
+          bad = true;  // never dereferenced: block 0 is read, the rows become NaN
+          id = 0;
+        }
+      }
+      bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+      return id;
+    };
+    int vid = load_ids();
+
+    auto issue = [&](uint4 (&kr)[KL], int buf, int j) {
+      const int t0 = p_lo + j * kT;
+      int b = t0 / BS - blk_base;
+      if (b + kIds - 1 >= 64) {  // past this batch of ids
+        blk_base += b;
+        b = 0;
+        vid = load_ids();
+      }
+      int ids[kIds];
+      ids[0] = __builtin_amdgcn_readlane(vid, b);
+#pragma unroll
+      for (int i = 1; i < kIds; ++i)
+        ids[i] = (t0 + i * BS < p_end) ? __builtin_amdgcn_readlane(vid, b + i) : ids[0];
+      tw.issue_ids(kr, buf, t0, p_end - 1, ids);
+    };
+
+    uint4 ka[KL], kb[KL];
+    issue(ka, 0, 0);
+    for (int j = 0;;) {
+      wait_vmem_all();
+      if (j + 1 < ntiles) issue(kb, 1, j + 1);
+      consume(ka, 0, p_lo + j * kT);
+      if (++j >= ntiles) break;
+      wait_vmem_all();
+      if (j + 1 < ntiles) issue(ka, 0, j + 1);
+      consume(kb, 1, p_lo + j * kT);
+      if (++j >= ntiles) break;
+    }
+    if constexpr (kGather) {
+      if (gathered == 0x9e3779b9u && lane == 0) out[0] = (uint16_t)gathered;
+    } else {
+      tw.finish();
+      write_result(tw, bad, row0, t_lo, t_hi, ns, g == g0, pair_start);
+    }
+
+    g += ntiles;
+    if (g >= g1) break;
+    // the run goes on, so this pair ended here: next pair
+    t_lo = 0;
+    if (++kh == hkv) {
+      kh = 0;
+      do {
+        if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
+        L = seq_lens[s];
+        ns = tiles_of(L);
+      } while (ns == 0);
+    }
+  }
+}
+
+// Merge of the partials of every (sequence, KV head) pair split between
+// waves, plus the rows no wave writes: zero rows for empty sequences, NaN
+// rows for lengths outside [0, max_blocks_per_seq * block_size].  One
+// workgroup per pair; a thread merges 4 consecutive elements of one query
+// head.  The length and the pair's record are loaded together, then the
+// partials four at a time with all their loads in flight at once.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
+                  const float2* __restrict__ ws_ml, const int4* __restrict__ ws_meta,
+                  const int32_t* __restrict__ seq_lens, int32_t hkv, int32_t max_len) {
+  constexpr int kBatch = 4;
+  const int pair = blockIdx.x;
+  const int s = pair / hkv, kh = pair % hkv;
+  const int64_t row0 = (int64_t)s * hkv * G + (int64_t)kh * G;
+  const int L = seq_lens[s];
+  const int4 meta = ws_meta[pair];  // meaningful only when L is in range
+  if (L <= 0 || L > max_len) {
+    const float v = L == 0 ? 0.0f : __builtin_nanf("");
+    for (int i = threadIdx.x; i < G * D; i += 256) out[row0 * D + i] = to_bits<T>(v);
+    return;
+  }
+  const int c_first = meta.x, c_last = meta.y;
+  if (c_first == c_last) return;  // finished by one wave
+  for (int i = threadIdx.x * 4; i < G * D; i += 256 * 4) {
+    const int h = i / D, d = i % D;
+    float M = kNegInf, den = 0.0f;
+    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = c_first; c0 <= c_last; c0 += kBatch) {
+      float2 ml[kBatch];
+      float4 a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + u;
+        ml[u] = make_float2(kNegInf, 0.0f);
+        a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c <= c_last) {
+          const int64_t slot = 2 * (int64_t)c + (c == c_first ? meta.z : 0);
+          ml[u] = ws_ml[slot * G + h];
+          a[u] = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
+      const float base = (Mb == kNegInf) ? 0.0f : Mb;
+      const float r = exp2_fast(M - base);  // rescale what is summed so far
+      den *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] *= r;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float f = exp2_fast(ml[u].x - base);
+        den = fmaf(f, ml[u].y, den);
+        num[0] = fmaf(f, a[u].x, num[0]);
+        num[1] = fmaf(f, a[u].y, num[1]);
+        num[2] = fmaf(f, a[u].z, num[2]);
+        num[3] = fmaf(f, a[u].w, num[3]);
+      }
+      M = Mb;
+    }
+    const uint2 o = make_uint2(pack2<T>(num[0] / den, num[1] / den),
+                               pack2<T>(num[2] / den, num[3] / den));
+    *reinterpret_cast<uint2*>(out + (row0 + h) * D + d) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Resident waves of one decode instantiation on the current device (cached
+// per instantiation and device; recomputing it gives the same value, so
+// concurrent first calls are harmless).
+template <typename T, typename KV, int D, int BS, int G>
+static int resident_waves() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cached = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (cached > 0) return cached;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, pa_decode_streamk<T, D, BS, G, false, KV>, kThreads, 0) != hipSuccess)
+    return 0;
+  const int waves = cus * max(per_cu, 1) * kWaves;
+  __atomic_store_n(&cache[dev], waves, __ATOMIC_RELAXED);
+  return waves;
+}
+
+template <typename T, typename KV, int D, int BS, int G>
+static hipError_t launch_t(const StreamKArgs& a, bool gather) {
+  using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
+  int waves = resident_waves<T, KV, D, BS, G>();
+  if (waves <= 0) return hipErrorInvalidDevice;
+  waves = min(waves, kStreamKMaxWaves) / kWaves * kWaves;
+  if (gather) {  // the same grid, gather-only (the group does not change the loads)
+    hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, 1, true, KV>), dim3((uint32_t)(waves / kWaves)),
+                       dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
+                       nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
+                       a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
+                       a.max_blocks_per_seq, a.num_blocks, waves, 0.0f, 0.0f);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>), dim3((uint32_t)(waves / kWaves)),
+                     dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
+                     (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
+                     a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
+                     a.max_blocks_per_seq, a.num_blocks, waves, a.qk_scale, a.out_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((pa_streamk_reduce<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),
+                     dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
+                     a.seq_lens, a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+  return hipGetLastError();
+}
+
+template <typename T, typename KV, int D, int BS>
+static hipError_t launch_g(const StreamKArgs& a, bool gather) {
+  switch (a.group) {
+    case 1: return launch_t<T, KV, D, BS, 1>(a, gather);
+    case 2: return launch_t<T, KV, D, BS, 2>(a, gather);
+    case 4: return launch_t<T, KV, D, BS, 4>(a, gather);
+    case 8: return launch_t<T, KV, D, BS, 8>(a, gather);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename KV, int D>
+static hipError_t launch_bs(const StreamKArgs& a, bool gather) {
+  switch (a.block_size) {
+    case 8: return launch_g<T, KV, D, 8>(a, gather);
+    case 16: return launch_g<T, KV, D, 16>(a, gather);
+    case 32: return launch_g<T, KV, D, 32>(a, gather);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename KV>
+static hipError_t launch_d(const StreamKArgs& a, bool gather) {
+  switch (a.head_dim) {
+    case 64: return launch_bs<T, KV, 64>(a, gather);
+    case 128: return launch_bs<T, KV, 128>(a, gather);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

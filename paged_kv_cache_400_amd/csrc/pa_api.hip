@@ -101,13 +101,21 @@ namespace {
 
 enum class Impl { kMfma, kValu };
 
+bool positive_finite(float x) { return x > 0.0f && x <= 3.4028234663852886e38f; }
+
+// kv_fp8: 8-bit E4M3 pools with scales k_scale / v_scale (pa_decode_fp8;
+// balanced split only).
 pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                       int32_t num_blocks, float scale, int32_t partition_size, pa_dtype dtype,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f) {
   g_last_error[0] = '\0';
+  if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale)))
+    return fail(PA_ERR_SHAPE, "pa_decode_fp8: k_scale %g and v_scale %g must be positive and "
+                "finite", (double)k_scale, (double)v_scale);
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PA_ERR_SHAPE,
@@ -174,10 +182,11 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
-    a.qk_scale = scale * 1.4426950408889634f;
+    a.qk_scale = scale * 1.4426950408889634f * (kv_fp8 ? k_scale : 1.0f);
+    a.out_scale = v_scale;
     a.bf16 = dtype == PA_BF16;
     a.stream = stream;
-    const hipError_t e = pa::launch_decode_streamk(a);
+    const hipError_t e = kv_fp8 ? pa::launch_decode_streamk_fp8(a) : pa::launch_decode_streamk(a);
     if (e != hipSuccess)
       return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
@@ -239,6 +248,59 @@ pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const vo
                      stream);
 }
 
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        float scale, float k_scale, float v_scale, pa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, scale, 0, dtype, workspace, workspace_bytes, stream, true,
+                     k_scale, v_scale);
+}
+
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                   void* v_cache, const int32_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, float k_scale,
+                                   float v_scale, pa_dtype dtype, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_reshape_and_cache_fp8: sizes must be positive (num_tokens >= 0): T=%d "
+                "Hkv=%d d=%d bs=%d NB=%d",
+                num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_fp8: dtype %d is not PA_F16 or "
+                "PA_BF16", (int)dtype);
+  if (!supported_cache_dims(head_dim, block_size) || head_dim % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_reshape_and_cache_fp8: head_dim %d (multiple of 16 in [16, 1024]) or "
+                "block_size %d (8, 16, 32) not supported",
+                head_dim, block_size);
+  if (!positive_finite(k_scale) || !positive_finite(v_scale))
+    return fail(PA_ERR_SHAPE, "pa_reshape_and_cache_fp8: k_scale %g and v_scale %g must be "
+                "positive and finite", (double)k_scale, (double)v_scale);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "pa_reshape_and_cache_fp8: a required pointer is NULL");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE,
+                "pa_reshape_and_cache_fp8: key, value and pools must be 16-byte aligned");
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 16);
+  if (total + 255 >= kMaxThreadsPerLaunch)
+    return fail(PA_ERR_SHAPE, "pa_reshape_and_cache_fp8: too many tokens for one launch");
+  const hipError_t e = pa::launch_reshape_and_cache_fp8(
+      key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+      num_blocks, k_scale, v_scale, dtype == PA_BF16, stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_reshape_and_cache_fp8: launch failed: %s",
+                hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -284,12 +346,13 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                 "pa_copy_blocks: sizes must be positive (num_pairs >= 0): n=%d Hkv=%d d=%d "
                 "bs=%d NB=%d",
                 num_pairs, num_kv_heads, head_dim, block_size, num_blocks);
-  if (dtype != PA_F16 && dtype != PA_BF16)
+  if (dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: dtype %d not supported", (int)dtype);
-  if (!supported_cache_dims(head_dim, block_size))
+  if (!supported_cache_dims(head_dim, block_size) ||
+      (dtype == PA_FP8_E4M3 && head_dim % 16 != 0))
     return fail(PA_ERR_UNSUPPORTED,
-                "pa_copy_blocks: head_dim %d (multiple of 8 in [8, 1024]) or block_size %d "
-                "(8, 16, 32) not supported",
+                "pa_copy_blocks: head_dim %d (multiple of 8 in [8, 1024], of 16 for 8-bit "
+                "pools) or block_size %d (8, 16, 32) not supported",
                 head_dim, block_size);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_mapping)
@@ -298,7 +361,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: pools must be 16-byte aligned");
   const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
                                               num_kv_heads, head_dim, block_size, num_blocks,
-                                              stream);
+                                              dtype == PA_FP8_E4M3 ? 1 : 2, stream);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
@@ -313,7 +376,7 @@ pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PA_ERR_SHAPE, "pa_probe_gather: sizes must be positive (num_seqs >= 0)");
-  if (dtype != PA_F16 && dtype != PA_BF16)
+  if (dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "pa_probe_gather: dtype %d not supported", (int)dtype);
   if ((head_dim != 64 && head_dim != 128) ||
       (block_size != 8 && block_size != 16 && block_size != 32))
@@ -346,7 +409,8 @@ pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
   a.num_blocks = num_blocks;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = pa::launch_gather_streamk(a);
+  const hipError_t e = dtype == PA_FP8_E4M3 ? pa::launch_gather_streamk_fp8(a)
+                                            : pa::launch_gather_streamk(a);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_probe_gather: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -41,8 +41,9 @@ struct StreamKArgs {
   int4* ws_meta;
   int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
   int32_t max_blocks_per_seq, num_blocks;
-  float qk_scale;
-  bool bf16;
+  float qk_scale;     // scale * log2(e) (* k_scale for 8-bit pools)
+  float out_scale;    // v_scale for 8-bit pools (unused for 16-bit pools)
+  bool bf16;          // q and out bf16 (else fp16)
   hipStream_t stream;
 };
 
@@ -62,6 +63,10 @@ hipError_t launch_decode_streamk(const StreamKArgs& a);
 // Gather-only run of the same split and loads (pa_probe_gather); uses only
 // out (a sink word), the pools, block_tables, seq_lens and the sizes.
 hipError_t launch_gather_streamk(const StreamKArgs& a);
+// The same over 8-bit E4M3 pools (decode_fp8.hip): pa_decode_fp8, and the
+// gather-only run on 8-bit pools.
+hipError_t launch_decode_streamk_fp8(const StreamKArgs& a);
+hipError_t launch_gather_streamk_fp8(const StreamKArgs& a);
 
 // pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
 // (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.
@@ -75,8 +80,18 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int32_t num_blocks, hipStream_t stream);
 
+// Quantising append into 8-bit E4M3 pools; key/value bf16 (bf16) or fp16.
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                        void* v_cache, const int32_t* slot_mapping,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float k_scale, float v_scale, bool bf16,
+                                        hipStream_t stream);
+
+// elem_bytes: 2 for 16-bit pools, 1 for 8-bit ones.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                               int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int32_t num_blocks, hipStream_t stream);
+                              int32_t block_size, int32_t num_blocks, int32_t elem_bytes,
+                              hipStream_t stream);
 
 }  // namespace pa

@@ -104,6 +104,14 @@ struct TileWave {
   using GE = Geo<D>;
   static constexpr int KC = GE::KC, NM = GE::NM;
   static_assert(G <= 16, "one MFMA row per query head");
+  // What the balanced driver needs to know of a tile wave.
+  using Out = T;                  // q and output type
+  using Elem = uint16_t;          // pool element
+  static constexpr int kD = D, kBS = BS, kG = G;
+  static constexpr int kTileLen = kTile;                  // positions per tile
+  static constexpr int KL = KC;                           // 16-byte K loads per lane
+  static constexpr int kIds = BS < kTile ? kTile / BS : 1;  // blocks per tile
+  static constexpr int kTileBytes = GE::TILE;             // one LDS V tile
 
   const uint16_t* kc;
   const uint16_t* vc;
@@ -176,6 +184,13 @@ struct TileWave {
             (void __attribute__((address_space(3)))*)(vt + i * GE::REGION), 16, 0,
             kCachePolicyStream);
     }
+  }
+
+  // The same, with the tile's block ids in an array (ids[j]: the block of
+  // positions t0 + j * BS ...).
+  __device__ __forceinline__ void issue_ids(uint4 (&kr)[KC], int buf, int t0, int t_last,
+                                            const int (&ids)[kIds]) {
+    issue(kr, buf, t0, t_last, ids[0], ids[kIds - 1]);
   }
 
   // Compute the tile at t0 (positions >= t_end masked) whose K is in kr and

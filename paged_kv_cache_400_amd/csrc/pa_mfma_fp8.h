@@ -1,0 +1,236 @@
+// pa_mfma_fp8.h -- TileWave8: the per-wave machinery of decode over 8-bit
+// KV pools (OCP FP8 E4M3 codes, one float32 scale per pool).  Same contract
+// as TileWave (pa_mfma.h) with a tile of 32 positions.
+//
+// Quantising the KV cache is the pages' lever on bytes per token ("What
+// problem does PagedAttention solve, and what is continuous batching?",
+// sections "Why the KV cache becomes the problem" and "What they'll ask
+// next"); they fix no format.  Every E4M3 value is exactly a bf16 and an
+// fp16 value, so codes are widened in registers (v_cvt_scalef32_pk_*_fp8,
+// scale 1) and the products run on the same 16-bit MFMAs as the 16-bit path;
+// k_scale is folded into the score scale and v_scale into the output by the
+// caller.
+//
+// Why 32 positions: at one byte per element a 16-position tile moves half
+// the bytes of the 16-bit one, and with one tile in flight per wave the HBM
+// queue would hold half as much.  A 32-position tile keeps the bytes per
+// wave in flight and makes P.V one 16x16x32 MFMA per 16 columns:
+//
+//  loads   K: the tile is two halves of 16 rows; lane l loads 16 bytes of
+//          row (half u, position l%16), d = 64c + 16*(l/16) .. +16, c < D/64.
+//          V: straight into the wave's LDS tile, stored as four regions of
+//          8 rows (region i: rows 4i..4i+3 of each half), 16 bytes of padding
+//          after each region so the four lane groups of a read hit disjoint
+//          banks.
+//  q.K^T   per half, D/32 v_mfma_f32_16x16x32: the 16 codes of a load are
+//          widened to two 8-element operands, the first for d = 64c +
+//          16*grp + 0..7 and the second for + 8..15; q is held in the same
+//          d order.  Lane l receives head l%16's scores for positions
+//          4*(l/16) + r of each half.
+//  P.V     D/16 v_mfma_f32_16x16x32 with the 32 positions on k in the order
+//          (half 0: 4*grp + 0..3, half 1: 4*grp + 0..3) for lane group grp:
+//          that is exactly what the lane holds of P after q.K^T, and exactly
+//          the 8 rows of region grp of the V tile, read as bytes and widened.
+#pragma once
+
+#include "pa_mfma.h"
+
+namespace pa {
+
+struct FP8 {};  // tag: pools of OCP E4M3 codes
+
+template <int D>
+struct Geo8 {
+  static constexpr int ROW = D;                 // bytes of one row
+  static constexpr int REGION = 8 * ROW + 16;   // 8 rows + padding
+  static constexpr int TILE = 4 * REGION;       // one LDS V tile
+  static constexpr int LANES = 8 * ROW / 16;    // lanes that fill a region
+};
+
+// Four E4M3 codes (one word) -> four 16-bit values in two words, exactly.
+template <typename T> __device__ __forceinline__ uint2 widen4(uint32_t w);
+template <> __device__ __forceinline__ uint2 widen4<BF16>(uint32_t w) {
+  return make_uint2(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+}
+template <> __device__ __forceinline__ uint2 widen4<F16>(uint32_t w) {
+  return make_uint2(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+}
+template <typename T> __device__ __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
+  const uint2 a = widen4<T>(w0), b = widen4<T>(w1);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+template <typename T, int D, int BS, int G>
+struct TileWave8 {
+  using GE = Geo8<D>;
+  using Out = T;
+  using Elem = uint8_t;
+  static_assert(G <= 16, "one MFMA row per query head");
+  static constexpr int kD = D, kBS = BS, kG = G;
+  static constexpr int kTileLen = 32;
+  static constexpr int KC = D / 32;              // q.K^T MFMA steps per half
+  static constexpr int KCH = D / 64;             // 16-byte K loads per half
+  static constexpr int KL = 2 * KCH;             // 16-byte K loads per lane per tile
+  static constexpr int NM = D / 16;              // P.V MFMAs
+  static constexpr int kIds = BS < kTileLen ? kTileLen / BS : 1;
+  static constexpr int kTileBytes = GE::TILE;
+
+  const uint8_t* kc;
+  const uint8_t* vc;
+  int64_t blk_stride;  // bytes per block of a pool
+  int64_t head_off;    // bytes to the KV head within a block
+  unsigned char* vtile;
+  int lane, col, grp;
+
+  uint4 qb[KC];      // q operand, step 2c + h: head col, d = 64c + 16 grp + 8h .. +8
+  f32x4_t acc[NM];   // P.V accumulators: head 4*grp + r, column 16*m + col
+  float m_run;       // running max of head col
+  float l_run;       // this lane's share of head col's denominator
+
+  __device__ __forceinline__ void init(const uint8_t* kc_, const uint8_t* vc_, int hkv, int kh,
+                                       unsigned char* vtile_) {
+    kc = kc_;
+    vc = vc_;
+    blk_stride = (int64_t)hkv * BS * D;
+    head_off = (int64_t)kh * BS * D;
+    vtile = vtile_;
+    lane = threadIdx.x & 63;
+    col = lane & 15;
+    grp = lane >> 4;
+  }
+
+  __device__ __forceinline__ void load_q(const uint16_t* q_rows) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        qb[2 * c + h] = make_uint4(0u, 0u, 0u, 0u);
+        if (col < G)
+          qb[2 * c + h] =
+              *reinterpret_cast<const uint4*>(q_rows + col * D + 64 * c + 16 * grp + 8 * h);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = kNegInf;
+    l_run = 0.0f;
+  }
+
+  // Block of position t (t0 <= t < t0 + 32) from the tile's ids.
+  __device__ __forceinline__ int block_of(int t, int t0, const int (&ids)[kIds]) const {
+    int id = ids[0];
+#pragma unroll
+    for (int j = 1; j < kIds; ++j)
+      if (t - t0 >= j * BS) id = ids[j];
+    return id;
+  }
+
+  // Issue the K (registers) and V (LDS buffer buf) loads of the tile at
+  // positions t0..t0+31, clamped to t_last; ids[j] is the block of positions
+  // t0 + j * BS ... (entries past t_last are not used).
+  __device__ __forceinline__ void issue_ids(uint4 (&kr)[KL], int buf, int t0, int t_last,
+                                            const int (&ids)[kIds]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = min(t0 + 16 * u + col, t_last);
+      const uint8_t* p = kc + (int64_t)block_of(t, t0, ids) * blk_stride + head_off +
+                         (t % BS) * D + grp * 16;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) kr[u * KCH + c] = load_stream(p + c * 64);
+    }
+    // V: lane l (< LANES) loads row r8 = l / (D/16) of region i, 16-byte
+    // chunk l % (D/16), landing at region i + 16 l bytes
+    unsigned char* vt = vtile + buf * GE::TILE;
+    const int r8 = lane / (D / 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = r8 < 4 ? 4 * i + r8 : 16 + 4 * i + (r8 - 4);
+      const int t = min(t0 + tau, t_last);
+      const uint8_t* vrow = vc + (int64_t)block_of(t, t0, ids) * blk_stride + head_off +
+                            (t % BS) * D;
+      if (GE::LANES == 64 || lane < GE::LANES)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vrow + (lane % (D / 16)) * 16),
+            (void __attribute__((address_space(3)))*)(vt + i * GE::REGION), 16, 0,
+            kCachePolicyStream);
+    }
+  }
+
+  __device__ __forceinline__ void consume(const uint4 (&kr)[KL], int buf, int t0, int t_end,
+                                          float qk_scale) {
+    f32x4_t sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const uint4 k8 = kr[u * KCH + c];
+        sc[u] = mfma_k32<T>(widen8<T>(k8.x, k8.y), qb[2 * c], sc[u]);
+        sc[u] = mfma_k32<T>(widen8<T>(k8.z, k8.w), qb[2 * c + 1], sc[u]);
+      }
+    }
+
+    float sr[8];
+    float lm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = (t0 + 16 * u + 4 * grp + r < t_end) ? sc[u][r] * qk_scale : kNegInf;
+        sr[4 * u + r] = v;
+        lm = fmaxf(lm, v);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(lm > m_run + kRescaleSlack) != 0) {
+      float mx = fmaxf(lm, __shfl_xor(lm, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = exp2_fast(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= corr;
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
+      }
+    }
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = pack2<T>(exp2_fast(sr[2 * j] - m_run), exp2_fast(sr[2 * j + 1] - m_run));
+      l_run += lo_f32<T>(p[j]) + hi_f32<T>(p[j]);
+    }
+    const uint4 pa_op = make_uint4(p[0], p[1], p[2], p[3]);
+
+    // B operand: the 8 rows of region grp at column 16 m + col
+    const unsigned char* vr = vtile + buf * GE::TILE + grp * GE::REGION + col;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned char* b = vr + 4 * h * GE::ROW + 16 * m;
+        w[h] = (uint32_t)b[0] | ((uint32_t)b[GE::ROW] << 8) | ((uint32_t)b[2 * GE::ROW] << 16) |
+               ((uint32_t)b[3 * GE::ROW] << 24);
+      }
+      acc[m] = mfma_k32<T>(pa_op, widen8<T>(w[0], w[1]), acc[m]);
+    }
+  }
+
+  __device__ __forceinline__ void finish() {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+  }
+};
+
+}  // namespace pa

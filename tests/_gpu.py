@@ -74,8 +74,11 @@ def half_ulp(ref, dtype):
     return np.ldexp(0.5, (e - bits).astype(np.int64))
 
 
-def compare(out_gpu, ref, pairs=None, label="", round_slack=False):
-    """Assert the attention tolerance; returns (max_abs, mean_abs)."""
+def compare(out_gpu, ref, pairs=None, label="", round_slack=False, value_scale=1.0):
+    """Assert the attention tolerance; returns (max_abs, mean_abs).
+    ``value_scale`` (>= 1) widens both bounds for values larger than unit
+    scale: the rounding of the softmax weights to the input type errs in
+    proportion to the values they weight."""
     got = out_gpu.detach().double().cpu().numpy()
     if pairs is not None:
         idx = np.asarray(pairs)
@@ -87,7 +90,8 @@ def compare(out_gpu, ref, pairs=None, label="", round_slack=False):
     if round_slack:
         err = np.maximum(err - half_ulp(ref, out_gpu.dtype), 0.0)
     mx = float(err.max())
-    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{label}: max-abs {mx:.3g} mean-abs {mean:.3g}"
+    assert mx <= MAX_ABS * value_scale and mean <= MEAN_ABS * value_scale, \
+        f"{label}: max-abs {mx:.3g} mean-abs {mean:.3g} (value scale {value_scale:g})"
     return mx, mean
 
 
@@ -101,3 +105,40 @@ def sample_pairs(b, n_seqs, seed=0):
     pick |= set(int(x) for x in rng.choice(rest, size=min(len(rest), n_seqs - len(pick)),
                                            replace=False))
     return np.array([(s, h) for s in sorted(pick) for h in range(b.num_q_heads)], np.int32)
+
+
+# ---- 8-bit (E4M3) pools
+
+def gpu_step_fp8(b, device="cuda:0", dev=None):
+    """copy_blocks -> quantising append -> decode_fp8 on the GPU; returns (out, dev)."""
+    dev = to_device(b, device) if dev is None else dev
+    if len(b.block_mapping):
+        pa.copy_blocks(dev["k_cache"], dev["v_cache"], dev["block_mapping"])
+    if len(b.slot_mapping):
+        pa.reshape_and_cache_fp8(dev["new_key"], dev["new_value"], dev["k_cache"],
+                                 dev["v_cache"], dev["slot_mapping"], b.k_scale, b.v_scale)
+    out = pa.decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                        dev["seq_lens"], b.k_scale, b.v_scale, scale=b.scale)
+    torch.cuda.synchronize()
+    return out, dev
+
+
+def oracle_pools_fp8(b):
+    """Host 8-bit pools after the step's copy and quantising append, by the oracle."""
+    kp, vp = b.k_cache.numpy().copy(), b.v_cache.numpy().copy()
+    if len(b.block_mapping):
+        oracle.copy_blocks_fp8(kp, vp, b.block_mapping)
+    if len(b.slot_mapping):
+        oracle.reshape_and_cache_fp8(bits(b.new_key), bits(b.new_value), kp, vp, b.slot_mapping,
+                                     b.k_scale, b.v_scale, ODT[b.dtype])
+    return kp, vp
+
+
+def oracle_out_fp8(b, kp, vp, pairs=None, lens=None):
+    return oracle.decode_fp8(bits(b.q), kp, vp, b.block_tables,
+                             b.seq_lens if lens is None else lens, b.scale, b.k_scale,
+                             b.v_scale, ODT[b.dtype], pairs=pairs)
+
+
+def pool_bytes(t):
+    return t.cpu().numpy()
