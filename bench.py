@@ -9,6 +9,11 @@ slot_mapping) + pa_decode over context + 1 (the decode kernel and, for the
 sequences longer than one 512-token partition, the log-sum-exp merge).
 Inputs are resident in HBM before timing starts.
 
+With --kv fp8 the same step runs over 8-bit OCP E4M3 K/V pools (one scale
+per pool): pa_reshape_and_cache_fp8 + pa_decode_fp8, B_kv counted at one byte
+per element.  The default (16-bit) run also times that step and adds it as
+the `fp8_kv` object.
+
 Prints one JSON line:
   value       effective KV GB/s of the whole step = B_kv / step time, with
               B_kv = sum_s L_s * 2 * Hkv * d * 2 bytes (live K and V read
@@ -42,10 +47,20 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per pa_decode call from the committed rocprofv3 FETCH_SIZE /
 # WRITE_SIZE summary; reported only while the kernel sources still hash to
 # the value recorded there (a changed kernel has no measured traffic).
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_streamk_mixed_step_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_400_amd", "csrc", f)
-                  for f in ("decode_streamk.hip", "pa_mfma.h", "pa_device.h", "pa_launch.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_cache_400_amd", "csrc")
+TRAFFIC_SUMMARY = {
+    "16": os.path.join(ROOT, "profiles", "pa_decode_streamk_mixed_step_traffic.md"),
+    "fp8": os.path.join(ROOT, "profiles", "pa_decode_fp8_mixed_step_traffic.md"),
+}
+KERNEL_SOURCES = {
+    "16": [os.path.join(_CSRC, f) for f in ("decode_streamk.hip", "decode_streamk.h",
+                                            "pa_mfma.h", "pa_device.h", "pa_launch.h")],
+    "fp8": [os.path.join(_CSRC, f) for f in ("decode_fp8.hip", "decode_streamk.h",
+                                             "pa_mfma_fp8.h", "pa_mfma.h", "pa_device.h",
+                                             "pa_launch.h")],
+}
 KERNEL_NAMES = {
+    ("fp8", True): "pa_decode_fp8 (pa_decode_streamk over E4M3 pools + pa_streamk_reduce)",
     ("mfma", True): "pa_decode (pa_decode_streamk + pa_streamk_reduce)",
     ("mfma", False): "pa_decode, explicit partitions (pa_decode_mfma + pa_splitk_reduce)",
     ("valu", True): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
@@ -53,25 +68,26 @@ KERNEL_NAMES = {
 }
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(kv="16"):
+    """SHA-256 over the sources the decode kernel of pool type kv is built from."""
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES[kv]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(kv="16"):
     """(bytes per call, note) from the counter summary, or (None, reason)."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(TRAFFIC_SUMMARY[kv]).read()
     except OSError:
         return None, "no counter summary"
     fields = dict(re.findall(r"^([a-z_0-9]+): (\S+)$", text, re.M))
-    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256(kv):
         return None, "kernel changed since the counters were taken"
-    return int(fields["traffic_bytes_per_call"]), os.path.relpath(TRAFFIC_SUMMARY, ROOT)
+    return int(fields["traffic_bytes_per_call"]), os.path.relpath(TRAFFIC_SUMMARY[kv], ROOT)
 
 
 def parse():
@@ -86,6 +102,11 @@ def parse():
                     help="minimum CPU time the oracle baseline accumulates")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="0: pa_decode's balanced split (stream-K); else explicit partitions")
+    ap.add_argument("--kv", choices=["16", "fp8"], default="16",
+                    help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
+                         "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
+    ap.add_argument("--fp8-summary", choices=["on", "off"], default="on",
+                    help="with --kv 16: also time the 8-bit step and add a summary object")
     ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
                     help="pa_decode (matrix-core kernel) or pa_decode_valu")
     ap.add_argument("--block-manager", choices=["on", "off"], default="on",
@@ -99,13 +120,25 @@ def parse():
 def cpu_baseline(b, seconds):
     import oracle
     from paged_kv_cache_400_amd.workload import bits
-    kp, vp = bits(b.k_cache).copy(), bits(b.v_cache).copy()
     nk, nv, q = bits(b.new_key), bits(b.new_value), bits(b.q)
+    if b.kv == "fp8":
+        kp, vp = b.k_cache.numpy().copy(), b.v_cache.numpy().copy()
+
+        def step():
+            oracle.reshape_and_cache_fp8(nk, nv, kp, vp, b.slot_mapping, b.k_scale, b.v_scale,
+                                         oracle.BF16)
+            oracle.decode_fp8(q, kp, vp, b.block_tables, b.seq_lens, b.scale, b.k_scale,
+                              b.v_scale, oracle.BF16)
+    else:
+        kp, vp = bits(b.k_cache).copy(), bits(b.v_cache).copy()
+
+        def step():
+            oracle.reshape_and_cache(nk, nv, kp, vp, b.slot_mapping)
+            oracle.decode(q, kp, vp, b.block_tables, b.seq_lens, b.scale, oracle.BF16)
     reps, total = 0, 0.0
     while reps == 0 or total < seconds:
         t0 = time.perf_counter()
-        oracle.reshape_and_cache(nk, nv, kp, vp, b.slot_mapping)
-        oracle.decode(q, kp, vp, b.block_tables, b.seq_lens, b.scale, oracle.BF16)
+        step()
         total += time.perf_counter() - t0
         reps += 1
     t = total / reps
@@ -150,34 +183,37 @@ def host_block_manager(b, steps=200):
             "ops": "append_batch (one token per sequence) + tables, through the Python binding"}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(b, dev, args, kv, partition_size, with_ceiling):
+    """Time K steps (append + decode) of batch b after W warmup steps, HIP
+    events on the current stream around the whole run and around each decode
+    call; then, optionally, K gather-only runs.  Returns (ms per step, ms per
+    decode call, ms per gather-only run or None)."""
     import torch
     import paged_kv_cache_400_amd as pa
-    from paged_kv_cache_400_amd import workload as wl
-
-    b = wl.make_mixed_step()
-    dev = wl.to_device(b, "cuda:0")
     S, Hq, d = b.q.shape
-    MB, bs = b.max_blocks_per_seq, b.block_size
-    ws_bytes = pa.decode_workspace_bytes(S, Hq, d, MB, bs, args.partition_size)
+    ws_bytes = pa.decode_workspace_bytes(S, Hq, d, b.max_blocks_per_seq, b.block_size,
+                                         partition_size)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
     out = torch.empty_like(dev["q"])
 
-    def append():
-        pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"], dev["v_cache"],
-                             dev["slot_mapping"])
+    if kv == "fp8":
+        def append():
+            pa.reshape_and_cache_fp8(dev["new_key"], dev["new_value"], dev["k_cache"],
+                                     dev["v_cache"], dev["slot_mapping"], b.k_scale, b.v_scale)
 
-    def decode():
-        pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
-                  scale=b.scale, partition_size=args.partition_size, out=out, workspace=ws,
-                  impl=args.impl)
+        def decode():
+            pa.decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                          dev["seq_lens"], b.k_scale, b.v_scale, scale=b.scale, out=out,
+                          workspace=ws)
+    else:
+        def append():
+            pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"],
+                                 dev["v_cache"], dev["slot_mapping"])
+
+        def decode():
+            pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                      dev["seq_lens"], scale=b.scale, partition_size=partition_size, out=out,
+                      workspace=ws, impl=args.impl)
 
     for _ in range(args.warmup):
         append()
@@ -202,7 +238,7 @@ def main():
 
     # the access pattern's own ceiling: the same K/V loads, nothing computed
     ceiling = None
-    if args.ceiling == "on":
+    if with_ceiling:
         sink = torch.zeros(2, dtype=torch.int16, device="cuda:0")
         for _ in range(args.warmup):
             pa.probe_gather(dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
@@ -216,6 +252,32 @@ def main():
         c1.record()
         torch.cuda.synchronize()
         ceiling = c0.elapsed_time(c1) / K
+    return ms_step, ms_decode, ceiling
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_400_amd as pa
+    from paged_kv_cache_400_amd import workload as wl
+
+    b = wl.make_mixed_step(kv=args.kv)
+    dev = wl.to_device(b, "cuda:0")
+    S, Hq, d = b.q.shape
+    MB, bs = b.max_blocks_per_seq, b.block_size
+    if args.kv == "fp8" and (args.partition_size != 0 or args.impl != "mfma"):
+        print("--kv fp8 runs pa_decode_fp8 (balanced split only)", file=sys.stderr)
+        sys.exit(2)
+    ms_step, ms_decode, ceiling = measure(b, dev, args, args.kv, args.partition_size,
+                                          args.ceiling == "on")
+    K = args.steps
+    fp8 = args.kv == "fp8"
 
     kv = b.kv_bytes()
     gbs_step = kv / (ms_step * 1e-3) / 1e9
@@ -231,12 +293,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 KV, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "mixed_step: 256 seqs, context uniform[64,4096] + 1 appended token, "
-                        "32 q / 8 kv heads, d 128, bf16 (f32 accumulate), block 16, "
-                        "shuffled pool of blocks+10%",
+            "workload": ("mixed_step_fp8: 256 seqs, context uniform[64,4096] + 1 appended "
+                         "token, 32 q / 8 kv heads, d 128, 8-bit E4M3 K/V pools (per-pool "
+                         "scale), bf16 q/out (f32 accumulate), block 16, shuffled pool of "
+                         "blocks+10%") if fp8 else
+                        ("mixed_step: 256 seqs, context uniform[64,4096] + 1 appended token, "
+                         "32 q / 8 kv heads, d 128, bf16 (f32 accumulate), block 16, "
+                         "shuffled pool of blocks+10%"),
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": b.num_kv_heads, "head_dim": d,
             "block_size": bs, "num_blocks": b.num_blocks, "max_blocks_per_seq": MB,
             "partition_size": args.partition_size or "balanced (stream-K)", "kv_bytes": kv,
@@ -247,7 +313,7 @@ def main():
         "decode_ms": round(ms_decode, 5),
         "decode_only_gbs": round(gbs_decode, 2),
         "roofline": {
-            "kernel": KERNEL_NAMES[(args.impl, args.partition_size == 0)],
+            "kernel": KERNEL_NAMES[("fp8" if fp8 else args.impl, args.partition_size == 0)],
             "bound": "hbm",
             "achieved": round(gbs_decode, 2),
             "peak": HBM_PEAK_GBS,
@@ -259,14 +325,14 @@ def main():
     if ceiling is not None:
         gbs_ceiling = kv / (ceiling * 1e-3) / 1e9
         res["roofline"]["achievable"] = {
-            "kernel": "pa_probe_gather: the same grid and K/V loads as pa_decode's balanced split, "
-                      "no arithmetic",
+            "kernel": "pa_probe_gather: the same grid and K/V loads as the decode's balanced "
+                      "split, no arithmetic",
             "us": round(ceiling * 1e3, 2), "gbs": round(gbs_ceiling, 2),
             "frac_of_peak": round(gbs_ceiling / HBM_PEAK_GBS, 4),
             "decode_frac_of_achievable": round(gbs_decode / gbs_ceiling, 4),
         }
     profiled = args.impl == "mfma" and args.partition_size == 0
-    traffic, note = measured_traffic()
+    traffic, note = measured_traffic(args.kv)
     if profiled and traffic is not None:
         res["roofline"]["traffic"] = traffic
         res["roofline"]["traffic_over_algorithmic"] = round(traffic / kv, 4)
@@ -286,6 +352,27 @@ def main():
                                    "gbs_read_plus_write": round(2 * n / (c0.elapsed_time(c1)
                                                                          * 1e-3) / 1e9, 1)}
         del src, dst
+    if args.kv == "16" and args.fp8_summary == "on" and profiled:
+        del dev
+        b8 = wl.make_mixed_step(kv="fp8")
+        dev8 = wl.to_device(b8, "cuda:0")
+        s8, d8, c8 = measure(b8, dev8, args, "fp8", 0, args.ceiling == "on")
+        kv8 = b8.kv_bytes()
+        res["fp8_kv"] = {
+            "workload": "the same step over 8-bit E4M3 K/V pools (bench.py --kv fp8)",
+            "kv_bytes": kv8,
+            "ms_per_step": round(s8, 5),
+            "value_gbs": round(kv8 / (s8 * 1e-3) / 1e9, 2),
+            "decode_ms": round(d8, 5),
+            "decode_gbs": round(kv8 / (d8 * 1e-3) / 1e9, 2),
+            "decode_frac_of_hbm_peak": round(kv8 / (d8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_seqs_per_s": round(S / (s8 * 1e-3), 1),
+            "step_speedup_vs_16bit": round(ms_step / s8, 3),
+        }
+        if c8 is not None:
+            res["fp8_kv"]["achievable_gbs"] = round(kv8 / (c8 * 1e-3) / 1e9, 2)
+            res["fp8_kv"]["decode_frac_of_achievable"] = round(c8 / d8, 4)
+        del dev8
     if args.block_manager == "on":
         res["host_block_manager"] = host_block_manager(b)
         res["host_block_manager"]["frac_of_step"] = round(

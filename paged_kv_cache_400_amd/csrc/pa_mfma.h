@@ -22,11 +22,10 @@
 //          ballot, so the usual tile needs no lane exchange and no rescale.
 //  P.V     acc[h][d] += sum_t P[h][t] V[t][d] as D/16 v_mfma_f32_16x16x16
 //          (A = P: the q.K^T result is already in the A layout; B = V with
-//          the 16 positions along k, read column-wise from LDS as 16-bit
-//          values).  The V tile is stored as four 4-row regions, each
-//          padded by 32 bytes, so the four lane groups of a read hit
-//          disjoint LDS banks and every read address is a lane base plus an
-//          immediate offset.
+//          the 16 positions along k).  The V tile is stored as four 4-row
+//          regions, each padded by 32 bytes; lane group g's B operand (rows
+//          4g..4g+3 of column 16 m + col) is one LDS transpose read
+//          (ds_read_b64_tr_b16) from region g.
 //  P is rounded to the input type for the P.V product and the softmax
 //  denominator sums the same rounded weights.  MFMA rows for heads >= G
 //  compute on zero queries and are never written.
@@ -229,16 +228,18 @@ struct TileWave {
     l_run += (lo_f32<T>(p01) + hi_f32<T>(p01)) + (lo_f32<T>(p23) + hi_f32<T>(p23));
     const uint2 pa_op = make_uint2(p01, p23);
 
-    // B operand: V[4*grp + r][16*m + col] from region grp, row r
-    const uint16_t* vr = reinterpret_cast<const uint16_t*>(vtile + buf * GE::TILE +
-                                                           grp * GE::REGION) + col;
+    // B operand: V[4*grp + r][16*m + col] from region grp, row r.
+    // ds_read_b64_tr_b16 transposes within each group of 16 lanes: lanes
+    // 4r .. 4r + 3 give row r (columns 16 m .. 16 m + 15, 4 each) and lane
+    // col receives element col of every row.
+    typedef short i16x4_t2 __attribute__((ext_vector_type(4)));
+    const unsigned char* vb = vtile + buf * GE::TILE + grp * GE::REGION + (col >> 2) * GE::ROW +
+                              8 * (col & 3);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const uint32_t b0 = vr[0 * D + 16 * m];
-      const uint32_t b1 = vr[1 * D + 16 * m];
-      const uint32_t b2 = vr[2 * D + 16 * m];
-      const uint32_t b3 = vr[3 * D + 16 * m];
-      acc[m] = mfma_k16<T>(pa_op, make_uint2(b0 | (b1 << 16), b2 | (b3 << 16)), acc[m]);
+      const i16x4_t2 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t2*)(vb + 32 * m));
+      acc[m] = mfma_k16<T>(pa_op, __builtin_bit_cast(uint2, w), acc[m]);
     }
   }
 

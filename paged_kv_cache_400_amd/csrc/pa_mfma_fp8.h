@@ -30,7 +30,11 @@
 //  P.V     D/16 v_mfma_f32_16x16x32 with the 32 positions on k in the order
 //          (half 0: 4*grp + 0..3, half 1: 4*grp + 0..3) for lane group grp:
 //          that is exactly what the lane holds of P after q.K^T, and exactly
-//          the 8 rows of region grp of the V tile, read as bytes and widened.
+//          the 8 rows of region grp of the V tile.  The B operand of MFMA m
+//          (the 8 rows' bytes of column 16 m + col) is one LDS transpose read
+//          (ds_read_b64_tr_b8) widened to 16 bits.  Reading it byte by byte
+//          instead costs 64 LDS reads per tile and 10% of the mixed decode
+//          step; reading whole rows and transposing in registers, 3%.
 #pragma once
 
 #include "pa_mfma.h"
@@ -212,18 +216,18 @@ struct TileWave8 {
     }
     const uint4 pa_op = make_uint4(p[0], p[1], p[2], p[3]);
 
-    // B operand: the 8 rows of region grp at column 16 m + col
-    const unsigned char* vr = vtile + buf * GE::TILE + grp * GE::REGION + col;
+    // B operand of MFMA m: V[row j of region grp][16 m + col], j = 0..7.
+    // ds_read_b64_tr_b8 transposes within each group of 16 lanes: lanes 2j
+    // and 2j + 1 give the two 8-byte halves of row j (columns 16 m ..
+    // 16 m + 15) and lane col receives byte col of every row.
+    typedef int i32x2_t __attribute__((ext_vector_type(2)));
+    const unsigned char* vb =
+        vtile + buf * GE::TILE + grp * GE::REGION + (col >> 1) * GE::ROW + 8 * (col & 1);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      uint32_t w[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned char* b = vr + 4 * h * GE::ROW + 16 * m;
-        w[h] = (uint32_t)b[0] | ((uint32_t)b[GE::ROW] << 8) | ((uint32_t)b[2 * GE::ROW] << 16) |
-               ((uint32_t)b[3 * GE::ROW] << 24);
-      }
-      acc[m] = mfma_k32<T>(pa_op, widen8<T>(w[0], w[1]), acc[m]);
+      const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * m));
+      acc[m] = mfma_k32<T>(pa_op, widen8<T>((uint32_t)w.x, (uint32_t)w.y), acc[m]);
     }
   }
 
