@@ -11,7 +11,8 @@ What is here:
     split-by-partition form merged by log-sum-exp, the append
     (reshape_and_cache), the copy-on-write block copy and the slot formula;
     for 8-bit pools (OCP E4M3, one scale per pool) the code <-> value maps,
-    the quantising append and decode over the dequantised pools.
+    the quantising append and decode over the dequantised pools; attention
+    of several causal query tokens per sequence (chunked prefill).
   * ``block_manager``: a plain-Python model of the host block manager.
   * ``accounting``: block counts and KV byte arithmetic of the worked memory
     example ("What problem does PagedAttention solve ...", section "A
@@ -67,9 +68,11 @@ def lib():
                                                    f32, f32, i32]
         L.oracle_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, f32, f32, f32, i32, vp, i32]
+        L.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32]
         for name in ("oracle_decode", "oracle_decode_split", "oracle_reshape_and_cache",
                      "oracle_copy_blocks", "oracle_slot_mapping", "oracle_quantize_e4m3",
-                     "oracle_reshape_and_cache_fp8", "oracle_decode_fp8"):
+                     "oracle_reshape_and_cache_fp8", "oracle_decode_fp8", "oracle_prefill"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -265,4 +268,24 @@ def decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_sc
                                    Hq, Hkv, d, bs, bt.shape[1], NB, float(np.float32(scale)),
                                    float(np.float32(k_scale)), float(np.float32(v_scale)),
                                    dtype, pp, npairs))
+    return out
+
+
+# ---- several query tokens per sequence (chunked prefill)
+
+def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, dtype):
+    """fp64 causal attention of chunk tokens: q [total_q][Hq][d] (uint16
+    patterns), query_start [S + 1]; token i of sequence s sits at position
+    seq_lens[s] - n_s + i and attends to positions <= its own.  Returns out
+    [total_q][Hq][d] float64."""
+    q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+    bt, sl, qs = _i32(block_tables), _i32(seq_lens), _i32(query_start)
+    T, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    S = sl.shape[0]
+    assert d2 == d and v_cache.shape == k_cache.shape and bt.shape[0] == S and qs.shape == (S + 1,)
+    out = np.full((T, Hq, d), np.nan, dtype=np.float64)
+    _check(lib().oracle_prefill(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(bt), _p(sl),
+                                _p(qs), S, T, Hq, Hkv, d, bs, bt.shape[1], NB,
+                                float(np.float32(scale)), dtype))
     return out

@@ -599,3 +599,94 @@ int oracle_decode_fp8(double* out, const uint16_t* q, const uint8_t* k_cache,
   }
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Several query tokens per sequence (chunked prefill).
+ *
+ * "What problem does PagedAttention solve, and what is continuous
+ * batching?" (datarekha): prefill is the first pass over the prompt
+ * ("Why the KV cache becomes the problem"), and production servers cap the
+ * tokens per scheduling step or split a long prompt into smaller pieces,
+ * chunked prefill ("How the two fit together in production").  Reading:
+ * a step hands sequence s a chunk of n_s = query_start[s+1] - query_start[s]
+ * new tokens whose keys and values are already in the pool, at positions
+ * L_s - n_s .. L_s - 1 (L_s = seq_lens[s], so 0 <= n_s <= L_s); token i of
+ * the chunk attends causally, to positions 0 .. L_s - n_s + i, through the
+ * sequence's block table.  n_s = 1 is decode; n_s = L_s is a whole prompt.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * out[query_start[s] + i][h][:] = softmax over t <= L_s - n_s + i of
+ * (scale * q[query_start[s] + i][h] . K_t) applied to V_t.
+ * q and out are [total_q][Hq][d] (q raw 16-bit patterns, out double);
+ * query_start has num_seqs + 1 non-decreasing entries from 0 to total_q.
+ */
+int oracle_prefill(double* out, const uint16_t* q, const uint16_t* k_cache,
+                   const uint16_t* v_cache, const int32_t* block_tables,
+                   const int32_t* seq_lens, const int32_t* query_start, int32_t num_seqs,
+                   int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                   int32_t num_blocks, float scale, int32_t dtype) {
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      num_q_heads % num_kv_heads != 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+    return ORACLE_BAD_ARG;
+  if (query_start[0] != 0 || query_start[num_seqs] != total_q) return ORACLE_BAD_ARG;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = query_start[s + 1] - query_start[s];
+    if (n < 0 || n > seq_lens[s]) return ORACLE_BAD_ARG;
+  }
+  int rc = check_tables(block_tables, seq_lens, num_seqs, max_blocks_per_seq, block_size,
+                        num_blocks);
+  if (rc != ORACLE_OK) return rc;
+  const int32_t group = num_q_heads / num_kv_heads;
+  int32_t max_len = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) max_len = seq_lens[s] > max_len ? seq_lens[s] : max_len;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
+    if (!z || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t k = 0; k < (int64_t)total_q * num_q_heads; ++k) {
+        const int32_t row = (int32_t)(k / num_q_heads), h = (int32_t)(k % num_q_heads);
+        int32_t s = 0;
+        while (query_start[s + 1] <= row) ++s;  /* the sequence this token belongs to */
+        const int32_t L = seq_lens[s], n = query_start[s + 1] - query_start[s];
+        const int32_t p = L - n + (row - query_start[s]);  /* its position */
+        const int32_t kh = h / group;
+        const uint16_t* qv = q + ((int64_t)row * num_q_heads + h) * head_dim;
+        double* o = out + ((int64_t)row * num_q_heads + h) * head_dim;
+        for (int32_t t = 0; t <= p; ++t) {
+          int64_t slot = slot_of(block_tables, max_blocks_per_seq, block_size, s, t);
+          int64_t b = slot / block_size, off = slot % block_size;
+          const uint16_t* kt = k_cache + ((b * num_kv_heads + kh) * block_size + off) * head_dim;
+          double dot = 0.0;
+          for (int32_t i = 0; i < head_dim; ++i) dot += widen(qv[i], dtype) * widen(kt[i], dtype);
+          z[t] = (double)scale * dot;
+        }
+        double m = -INFINITY;
+        for (int32_t t = 0; t <= p; ++t) m = z[t] > m ? z[t] : m;
+        double l = 0.0;
+        for (int32_t i = 0; i < head_dim; ++i) acc[i] = 0.0;
+        for (int32_t t = 0; t <= p; ++t) {
+          double w = exp(z[t] - m);
+          l += w;
+          int64_t slot = slot_of(block_tables, max_blocks_per_seq, block_size, s, t);
+          int64_t b = slot / block_size, off = slot % block_size;
+          const uint16_t* vt = v_cache + ((b * num_kv_heads + kh) * block_size + off) * head_dim;
+          for (int32_t i = 0; i < head_dim; ++i) acc[i] += w * widen(vt[i], dtype);
+        }
+        for (int32_t i = 0; i < head_dim; ++i) o[i] = acc[i] / l;
+      }
+    }
+    free(z);
+    free(acc);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}

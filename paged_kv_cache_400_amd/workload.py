@@ -27,7 +27,9 @@ them:
   * ``[seed, 6, s]``   8-bit pools: sequence s's K codes then V codes for
                        the positions already in the pool;
   * ``[seed, 7, s]``   8-bit pools: its 16-bit K rows then V rows for the
-                       positions the step appends.
+                       positions the step appends;
+  * ``[seed, 8]``      chunked prefill: the queries of every chunk token,
+                       [total_q][Hq][d].
 Values are float32 standard normal rounded to fp16/bf16 by
 round-to-nearest-even.
 Pool slots that hold no token are NaN (0x7E00 fp16, 0x7FC0 bf16); table
@@ -81,13 +83,14 @@ class PagedBatch:
     block_mapping: np.ndarray        # int32 [n][2] (src, dst)
     poison_block: int                # a NaN block no sequence owns
     info: Dict = field(default_factory=dict)
+    query_start: Optional[np.ndarray] = None  # chunked prefill: int32 [S + 1]; q is [total_q][Hq][d]
     kv: str = "16"                   # "16": pools of `dtype`; "fp8": E4M3 codes (uint8)
     k_scale: float = 1.0             # 8-bit pools: value of a key code = e4m3(code) * k_scale
     v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
-        return int(self.q.shape[0])
+        return int(len(self.seq_lens))
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -212,9 +215,9 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
                       v_scale: float = FP8_DEFAULT_SCALE) -> PagedBatch:
     """A batch of independent sequences (no sharing).
 
-    ``context_lens[s]`` tokens are already in the pool; ``append`` (0 or 1)
-    new tokens per sequence are appended by the step, so decode attends over
-    context + append.  Blocks for the context are taken from the free list in
+    ``context_lens[s]`` tokens are already in the pool; ``append`` (a count,
+    or one count per sequence) new tokens per sequence are appended by the
+    step, so decode attends over context + append.  Blocks for the context are taken from the free list in
     sequence order, then blocks attached by the append.  ``pad_tokens`` extra
     new-token rows with slot -1 are interleaved (the append skips them).
     ``placement_seed`` (default ``seed``) changes only where blocks go.
@@ -448,6 +451,36 @@ def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
                       poison_block=poison,
                       info={"shared_blocks": shared.copy(), "r": r, "tails": tails,
                             "prefix": prefix})
+
+
+def make_prefill_batch(name: str, context_lens, chunk_lens, num_q_heads: int,
+                       num_kv_heads: int, head_dim: int, block_size: int, dtype: str,
+                       seed: int, **kw) -> PagedBatch:
+    """Chunked prefill: sequence s has context_lens[s] tokens in the pool and
+    a chunk of chunk_lens[s] new tokens that the step appends (slot_mapping,
+    new_key, new_value) and then attends with, causally: chunk token i sits
+    at position context + i.  q holds one row per chunk token, [total_q][Hq]
+    [d] from stream [seed, 8]; query_start[s] is sequence s's first row."""
+    chunks = np.asarray(chunk_lens, dtype=np.int32)
+    b = make_decode_batch(name, context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                          dtype, seed, append=chunks, **kw)
+    T = int(chunks.sum())
+    b.q = _round(np.random.default_rng([seed, 8]).standard_normal((T, num_q_heads, head_dim),
+                                                                  dtype=np.float32), dtype)
+    b.query_start = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return b
+
+
+def make_chunked_prefill(seed: int = 6, num_seqs: int = 32, chunk: int = 512, lo: int = 1024,
+                         hi: int = 4096, dtype: str = "bf16") -> PagedBatch:
+    """Chunked-prefill step: 32 sequences with total lengths uniform in
+    [1024, 4096] whose last 512 tokens are this step's chunk, 32 q / 8 KV
+    heads, d 128, bf16, block 16, pool of total blocks + 10% from a seeded
+    shuffled free list."""
+    lens = mixed_lengths(num_seqs, lo, hi, seed)
+    chunks = np.full(num_seqs, chunk, dtype=np.int32)
+    return make_prefill_batch("chunked_prefill", lens - chunks, chunks, 32, 8, 128, 16, dtype,
+                              seed)
 
 
 WORKLOADS = {
