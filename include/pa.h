@@ -222,6 +222,49 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
                                    int32_t block_size, int32_t num_blocks, float k_scale,
                                    float v_scale, pa_dtype dtype, hipStream_t stream);
 
+/*
+ * Several query tokens per sequence with a causal mask (chunked prefill).
+ * The pages describe prefill as the compute-heavy first pass over a prompt
+ * and chunked prefill as splitting a long prompt into pieces processed over
+ * several steps ("What problem does PagedAttention solve, and what is
+ * continuous batching?", sections "Why the KV cache becomes the problem"
+ * and "How the two fit together in production").
+ *
+ * Sequence s has a chunk of n_s = query_start[s+1] - query_start[s] tokens
+ * whose keys and values are already in the pools (pa_reshape_and_cache),
+ * at positions L_s - n_s .. L_s - 1 (L_s = seq_lens[s]).  For chunk token i
+ * and query head h:
+ *
+ *   out[query_start[s] + i][h][:] =
+ *       sum_{t <= L_s - n_s + i} softmax_t(scale * q[query_start[s] + i][h] . K_t) V_t
+ *
+ * with K_t, V_t read through block_tables[s] from KV head h / (num_q_heads /
+ * num_kv_heads).  n_s = 1 is decode; n_s = L_s is a whole prompt; n_s = 0
+ * writes nothing.  q and out are [total_q][num_q_heads][head_dim];
+ * query_start holds num_seqs + 1 non-decreasing offsets from 0 to total_q
+ * (device memory).  Arithmetic as pa_decode (float32 scores and sums,
+ * softmax weights rounded to dtype for P.V, out rounded to dtype).
+ *
+ * Supported: dtype F16/BF16; head_dim 64 or 128; block_size 8, 16 or 32;
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}.  No workspace.
+ *
+ * Device data that breaks the contract is never dereferenced: a chunk
+ * longer than its sequence, a length past the block table or a block id
+ * outside the pool gives NaN rows for that sequence's chunk; offsets that
+ * are not non-decreasing within [0, total_q] give an empty chunk (its rows
+ * are left unwritten).  Rows outside [0, total_q) are never accessed.
+ *
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, num_q_heads not a
+ * multiple of num_kv_heads, misaligned pointer, too many rows for one
+ * launch), PA_ERR_UNSUPPORTED, PA_ERR_HIP.
+ */
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t total_q,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                     float scale, pa_dtype dtype, hipStream_t stream);
+
 /* Static name of a status code. */
 const char* pa_status_string(pa_status status);
 

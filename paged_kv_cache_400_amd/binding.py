@@ -35,6 +35,8 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _f32, _f32, _f32, ctypes.c_int, _vp, _sz,
                                      _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _f32, ctypes.c_int, _vp]),
     "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                                 _i32, _f32, _f32, ctypes.c_int, _vp]),
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -163,6 +165,41 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_si
     _check(fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
               _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB, float(scale),
               int(partition_size), _DT[q.dtype], _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale=None, out=None):
+    """Causal attention of several query tokens per sequence (chunked
+    prefill): q [total_q][Hq][d]; query_start int32 [S + 1] (chunk offsets);
+    chunk token i of sequence s sits at position seq_lens[s] - n_s + i and
+    attends to positions <= its own."""
+    _need(q, "q", 3)
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    _need(k_cache, "k_cache", 4, q.dtype, dev)
+    _need(v_cache, "v_cache", 4, q.dtype, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    _need(query_start, "query_start", 1, torch.int32, dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    T, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    S = seq_lens.shape[0]
+    if d2 != d or block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("inconsistent shapes between q, the pools, block_tables, seq_lens and "
+                         "query_start")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", 3, q.dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(_lib.pa_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                           _ptr(seq_lens), _ptr(query_start), S, T, Hq, Hkv, d, bs,
+                           block_tables.shape[1], NB, float(scale), _DT[q.dtype], _stream(dev)))
     return out
 
 

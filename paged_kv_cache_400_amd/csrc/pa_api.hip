@@ -301,6 +301,65 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
   return PA_OK;
 }
 
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t total_q,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                     float scale, pa_dtype dtype, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE,
+                "pa_prefill: sizes must be positive (num_seqs, total_q >= 0): S=%d T=%d Hq=%d "
+                "Hkv=%d d=%d bs=%d MB=%d NB=%d",
+                num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, block_size,
+                max_blocks_per_seq, num_blocks);
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: dtype %d is not PA_F16 or PA_BF16", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d not in {64, 128}", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d not in {8, 16, 32}", block_size);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: query group %d not in {1, 2, 4, 8}", group);
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start)
+    return fail(PA_ERR_NULL, "pa_prefill: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE, "pa_prefill: out, q, k_cache and v_cache must be 16-byte aligned");
+  const int64_t units = pa::prefill_units(total_q, num_seqs, num_kv_heads, group);
+  if (units * 64 >= kMaxThreadsPerLaunch)
+    return fail(PA_ERR_SHAPE, "pa_prefill: %lld work units exceed one launch", (long long)units);
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.qk_scale = scale * 1.4426950408889634f;
+  a.bf16 = dtype == PA_BF16;
+  a.stream = stream;
+  const hipError_t e = pa::launch_prefill(a);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_prefill: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -68,6 +68,26 @@ hipError_t launch_gather_streamk(const StreamKArgs& a);
 hipError_t launch_decode_streamk_fp8(const StreamKArgs& a);
 hipError_t launch_gather_streamk_fp8(const StreamKArgs& a);
 
+// Chunked prefill (prefill.hip): one wave per (sequence, KV head, 16 query
+// rows), causal within each chunk; no workspace.
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start;
+  int32_t num_seqs, total_q, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq, num_blocks;
+  float qk_scale;  // scale * log2(e)
+  bool bf16;
+  hipStream_t stream;
+};
+hipError_t launch_prefill(const PrefillArgs& a);
+// Waves the prefill launch has (an upper bound on its units).
+int64_t prefill_units(int32_t total_q, int32_t num_seqs, int32_t num_kv_heads, int32_t group);
+
 // pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
 // (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.
 hipError_t launch_decode(const DecodeArgs& a);
