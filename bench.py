@@ -9,6 +9,11 @@ slot_mapping) + pa_decode over context + 1 (the decode kernel and, for the
 sequences longer than one 512-token partition, the log-sum-exp merge).
 Inputs are resident in HBM before timing starts.
 
+With --mode prefill the line is the chunked-prefill step instead (32
+sequences whose last 512 tokens are this step's chunk; append + pa_prefill),
+in TFLOP/s of useful causal FLOPs against the bf16 matrix-core peak; the
+default run adds it as the `chunked_prefill` object.
+
 With --kv fp8 the same step runs over 8-bit OCP E4M3 K/V pools (one scale
 per pool): pa_reshape_and_cache_fp8 + pa_decode_fp8, B_kv counted at one byte
 per element.  The default (16-bit) run also times that step and adds it as
@@ -68,6 +73,22 @@ KERNEL_NAMES = {
 }
 
 
+def prefill_flops(seq_lens, query_start, num_q_heads: int, head_dim: int) -> int:
+    """Useful floating-point operations of causal chunk attention: for each
+    chunk token at position p and each query head, (p + 1) positions of a
+    q.K dot product and of a P.V accumulation, 2 * d each."""
+    import numpy as np
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    qs = np.asarray(query_start, dtype=np.int64)
+    n = qs[1:] - qs[:-1]
+    # sum over i < n of (L - n + i + 1) = n (L - n + 1) + n (n - 1) / 2
+    pos = n * (lens - n + 1) + n * (n - 1) // 2
+    return int(pos.sum()) * num_q_heads * 4 * head_dim
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
 def kernel_sources_sha256(kv="16"):
     """SHA-256 over the sources the decode kernel of pool type kv is built from."""
     import hashlib
@@ -105,6 +126,12 @@ def parse():
     ap.add_argument("--kv", choices=["16", "fp8"], default="16",
                     help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
                          "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
+    ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
+                    help="decode: the mixed decode step (the headline); prefill: the chunked "
+                         "prefill step (32 sequences x 512-token chunks, pa_prefill)")
+    ap.add_argument("--prefill-summary", choices=["on", "off"], default="on",
+                    help="with --mode decode: also time the chunked-prefill step and add a "
+                         "summary object")
     ap.add_argument("--fp8-summary", choices=["on", "off"], default="on",
                     help="with --kv 16: also time the 8-bit step and add a summary object")
     ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
@@ -255,6 +282,103 @@ def measure(b, dev, args, kv, partition_size, with_ceiling):
     return ms_step, ms_decode, ceiling
 
 
+def measure_prefill(b, dev, args):
+    """K steps of the chunked-prefill step (append of the chunks' keys and
+    values + pa_prefill) after W warmup steps; HIP events on the current
+    stream around the whole run and around each pa_prefill call.  Returns
+    (ms per step, ms per pa_prefill call)."""
+    import torch
+    import paged_kv_cache_400_amd as pa
+    qs = torch.from_numpy(b.query_start).to("cuda:0")
+    out = torch.empty_like(dev["q"])
+
+    def append():
+        pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"], dev["v_cache"],
+                             dev["slot_mapping"])
+
+    def attend():
+        pa.prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                   dev["seq_lens"], qs, scale=b.scale, out=out)
+
+    for _ in range(args.warmup):
+        append()
+        attend()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        append()
+        ev[i][0].record()
+        attend()
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K, sum(a.elapsed_time(z) for a, z in ev) / K
+
+
+PREFILL_WORKLOAD = ("chunked_prefill: 32 seqs, total length uniform[1024,4096] whose last 512 "
+                    "tokens are this step's chunk (16384 query tokens), causal, 32 q / 8 kv "
+                    "heads, d 128, bf16 (f32 accumulate), block 16, shuffled pool of blocks+10%")
+
+
+def prefill_line(args):
+    import torch
+    from paged_kv_cache_400_amd import workload as wl
+    b = wl.make_chunked_prefill()
+    dev = wl.to_device(b, "cuda:0")
+    ms_step, ms_attend = measure_prefill(b, dev, args)
+    fl = prefill_flops(b.seq_lens, b.query_start, b.num_q_heads, b.head_dim)
+    tq = int(b.query_start[-1])
+    tf = fl / (ms_attend * 1e-3) / 1e12
+    res = {
+        "metric": "chunked prefill attention TFLOP/s (causal useful FLOPs) + tokens/s",
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL_WORKLOAD, "num_seqs": b.num_seqs, "query_tokens": tq,
+                   "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+                   "head_dim": b.head_dim, "block_size": b.block_size, "flops": fl,
+                   "kv_bytes": b.kv_bytes()},
+        "prefill_ms": round(ms_attend, 5),
+        "prefill_tokens_per_s": round(tq / (ms_step * 1e-3), 1),
+        "roofline": {"kernel": "pa_prefill (pa_prefill_kernel)", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "traffic_source": "not profiled"},
+    }
+    if args.cpu_baseline == "on":
+        import oracle
+        from paged_kv_cache_400_amd.workload import bits
+        kp, vp = bits(b.k_cache).copy(), bits(b.v_cache).copy()
+        oracle.reshape_and_cache(bits(b.new_key), bits(b.new_value), kp, vp, b.slot_mapping)
+        # a bounded sample: the first 4 sequences' chunks
+        sub = 4
+        qe = int(b.query_start[sub])
+        t0 = time.perf_counter()
+        oracle.prefill(bits(b.q)[:qe], kp, vp, b.block_tables[:sub], b.seq_lens[:sub],
+                       b.query_start[:sub + 1], b.scale, oracle.BF16)
+        t = time.perf_counter() - t0
+        fl_sub = prefill_flops(b.seq_lens[:sub], b.query_start[:sub + 1], b.num_q_heads,
+                               b.head_dim)
+        res["cpu_baseline"] = {"value": round(fl_sub / t / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"the chunks of the first {sub} sequences ({qe} query "
+                                         f"tokens, all heads), float64, one run of {t:.2f} s"}
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -266,6 +390,10 @@ def main():
     import torch
     import paged_kv_cache_400_amd as pa
     from paged_kv_cache_400_amd import workload as wl
+
+    if args.mode == "prefill":
+        print(json.dumps(prefill_line(args)), flush=True)
+        return
 
     b = wl.make_mixed_step(kv=args.kv)
     dev = wl.to_device(b, "cuda:0")
@@ -373,6 +501,19 @@ def main():
             res["fp8_kv"]["achievable_gbs"] = round(kv8 / (c8 * 1e-3) / 1e9, 2)
             res["fp8_kv"]["decode_frac_of_achievable"] = round(c8 / d8, 4)
         del dev8
+    if args.prefill_summary == "on" and profiled and args.kv == "16":
+        pf = wl.make_chunked_prefill()
+        devp = wl.to_device(pf, "cuda:0")
+        sp, ap = measure_prefill(pf, devp, args)
+        fl = prefill_flops(pf.seq_lens, pf.query_start, pf.num_q_heads, pf.head_dim)
+        res["chunked_prefill"] = {
+            "workload": PREFILL_WORKLOAD + " (bench.py --mode prefill)",
+            "flops": fl, "prefill_ms": round(ap, 5), "ms_per_step": round(sp, 5),
+            "tflops": round(fl / (ap * 1e-3) / 1e12, 2),
+            "frac_of_mfma_bf16_peak": round(fl / (ap * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(int(pf.query_start[-1]) / (sp * 1e-3), 1),
+        }
+        del devp
     if args.block_manager == "on":
         res["host_block_manager"] = host_block_manager(b)
         res["host_block_manager"]["frac_of_step"] = round(
