@@ -14,6 +14,13 @@ sequences whose last 512 tokens are this step's chunk; append + pa_prefill),
 in TFLOP/s of useful causal FLOPs against the bf16 matrix-core peak; the
 default run adds it as the `chunked_prefill` object.
 
+With --mode serve the line is this build's own measurement of what the
+pages credit paged allocation with: an iteration-level batching loop (host
+scheduler + block manager + the kernels) over one pool, admitting by free
+blocks, against the same loop holding 4096-token reservations; generated
+tokens per second of summed kernel time and of wall time, and the mean
+decode batch, for both.
+
 With --kv fp8 the same step runs over 8-bit OCP E4M3 K/V pools (one scale
 per pool): pa_reshape_and_cache_fp8 + pa_decode_fp8, B_kv counted at one byte
 per element.  The default (16-bit) run also times that step and adds it as
@@ -126,9 +133,13 @@ def parse():
     ap.add_argument("--kv", choices=["16", "fp8"], default="16",
                     help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
                          "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
-    ap.add_argument("--mode", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "serve"], default="decode",
                     help="decode: the mixed decode step (the headline); prefill: the chunked "
-                         "prefill step (32 sequences x 512-token chunks, pa_prefill)")
+                         "prefill step (32 sequences x 512-token chunks, pa_prefill); serve: "
+                         "iteration-level batching over the paged pool against 4096-token "
+                         "reservations on the same pool")
+    ap.add_argument("--serve-iterations", type=int, default=300,
+                    help="timed iterations per policy in --mode serve (after as many untimed)")
     ap.add_argument("--prefill-summary", choices=["on", "off"], default="on",
                     help="with --mode decode: also time the chunked-prefill step and add a "
                          "summary object")
@@ -379,6 +390,52 @@ def prefill_line(args):
     return res
 
 
+SERVE_WORKLOAD = ("serve: a seeded stream of requests (prompts uniform[64,1024], generations "
+                  "uniform[16,512], 8 arrivals per iteration), one attention layer of 32 q / 8 kv "
+                  "heads, d 128, bf16, a pool of 4096 16-token blocks (65,536 tokens), at most "
+                  "256 running requests and 2048 prefill tokens per iteration")
+
+
+def serve_line(args):
+    """Iteration-level batching driven through the kernels: the paged pool
+    (admit by free blocks, grow block by block) against 4096-token
+    reservations on the same pool.  Each policy runs W untimed iterations
+    (the ramp-up), then K timed ones."""
+    from paged_kv_cache_400_amd.scheduler import Executor, Scheduler, seeded_requests
+    nb, K = 4096, args.serve_iterations
+    res = {}
+    for mode in ("paged", "reserved"):
+        reqs = seeded_requests(20000, seed=6, prompt=(64, 1024), gen=(16, 512), rate=8.0)
+        sched = Scheduler(mode, reqs, num_blocks=nb, block_size=16, max_batch=256,
+                          max_step_tokens=2048)
+        ex = Executor(nb, 16, 32, 8, 128, seed=6)
+        ex.run(sched, K)
+        st = ex.run(sched, K, timed=True)
+        res[mode] = {
+            "generated_tokens": st["generated_tokens"], "iterations": st["iterations"],
+            "mean_decode_batch": round(st["generated_tokens"] / st["iterations"], 2),
+            "prefill_tokens": st["prefill_tokens"],
+            "kernel_ms": round(st["kernel_ms"], 3), "wall_s": round(st["wall_s"], 3),
+            "tokens_per_kernel_s": round(st["generated_tokens"] / (st["kernel_ms"] * 1e-3), 1),
+            "tokens_per_wall_s": round(st["generated_tokens"] / st["wall_s"], 1),
+            "kernel_ms_per_iteration": round(st["kernel_ms"] / st["iterations"], 4),
+        }
+    p, r = res["paged"], res["reserved"]
+    return {
+        "metric": "generated tokens/s of kernel time under iteration-level batching "
+                  "(paged pool vs 4096-token reservations)",
+        "value": p["tokens_per_kernel_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": K, "ms_per_step": p["kernel_ms_per_iteration"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": SERVE_WORKLOAD, "num_blocks": nb, "block_size": 16},
+        "paged": p, "reserved": r,
+        "paged_over_reserved": {
+            "decode_batch": round(p["mean_decode_batch"] / r["mean_decode_batch"], 3),
+            "tokens_per_kernel_s": round(p["tokens_per_kernel_s"] / r["tokens_per_kernel_s"], 3),
+            "tokens_per_wall_s": round(p["tokens_per_wall_s"] / r["tokens_per_wall_s"], 3)},
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -393,6 +450,9 @@ def main():
 
     if args.mode == "prefill":
         print(json.dumps(prefill_line(args)), flush=True)
+        return
+    if args.mode == "serve":
+        print(json.dumps(serve_line(args)), flush=True)
         return
 
     b = wl.make_mixed_step(kv=args.kv)

@@ -1,0 +1,73 @@
+"""The iteration-level scheduler driving the library on the GPU: requests
+arrive, are admitted as the paged pool allows, prefill in chunks under a
+per-step token cap (pa_prefill), decode one token per iteration
+(pa_decode), are preempted when the pool runs dry and finish, with every
+token placed by the host block manager.
+
+Checked after every iteration: the prefill and decode outputs against the
+float64 oracle on host copies of the pools (attention tolerance), and,
+independently of kernels and oracle, that each live request's keys and
+values read through its block table are exactly its own rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import compare
+from paged_kv_cache_400_amd.scheduler import Executor, Scheduler, seeded_requests
+from paged_kv_cache_400_amd.workload import bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mode", ["paged", "reserved", "static"])
+def test_scheduler_drives_prefill_and_decode(mode):
+    nb, bs = 48, 16
+    reqs = seeded_requests(14, seed=5, prompt=(20, 200), gen=(3, 40), rate=1.5)
+    kw = dict(block_size=bs, max_batch=8, max_step_tokens=64)
+    if mode == "paged":
+        sched = Scheduler("paged", reqs, num_blocks=nb, **kw)
+    else:   # reservations of 256 tokens: 3 fit the pool
+        sched = Scheduler(mode, reqs, num_blocks=nb, reserve_tokens=256, **kw)
+    ex = Executor(nb, bs, num_q_heads=8, num_kv_heads=2, head_dim=64, seed=7)
+    kt, vt = bits(ex.kv_table[:, 0].contiguous()), bits(ex.kv_table[:, 1].contiguous())
+    counts = dict(prefill=0, decode=0, preempted=0)
+
+    def observe(it, plan, info):
+        torch.cuda.synchronize()
+        kp, vp = bits(ex.k_cache.cpu()), bits(ex.v_cache.cpu())
+        if "prefill" in info:
+            rids, q, qs, bt, lens, out = info["prefill"]
+            ref = oracle.prefill(bits(q.cpu()), kp, vp, bt, lens, np.asarray(qs, np.int32),
+                                 ex.scale, oracle.BF16)
+            compare(out, ref, label=f"{mode} it {it} prefill", round_slack=True)
+            counts["prefill"] += 1
+        if "decode" in info:
+            rids, q, bt, lens, out = info["decode"]
+            ref = oracle.decode(bits(q.cpu()), kp, vp, bt, lens, ex.scale, oracle.BF16)
+            compare(out, ref, label=f"{mode} it {it} decode", round_slack=True)
+            counts["decode"] += 1
+        counts["preempted"] += len(plan.preempted)
+        # every live request's rows are where its table says
+        for rid, L in ex.kv_len.items():
+            t, lens = ex.bm.tables([rid], -(-L // bs))
+            pos = np.arange(L)
+            blk, off = t[0, pos // bs], pos % bs
+            rows = ex.row_of(rid, pos)
+            assert np.array_equal(kp[blk, :, off, :], kt[rows]), f"it {it} rid {rid} keys"
+            assert np.array_equal(vp[blk, :, off, :], vt[rows]), f"it {it} rid {rid} values"
+        # the manager's free count is the pool minus the live requests' blocks
+        assert ex.bm.num_free() == nb - sum(-(-L // bs) for L in ex.kv_len.values())
+
+    stats = ex.run(sched, 10_000, observe=observe)
+    assert len(sched.done) == len(reqs) and not ex.kv_len
+    assert counts["prefill"] > 0 and counts["decode"] > 0
+    # tokens generated before a preemption are generated again after it
+    if counts["preempted"]:
+        assert stats["generated_tokens"] > sum(r.gen_len for r in reqs)
+    else:
+        assert stats["generated_tokens"] == sum(r.gen_len for r in reqs)
+    if mode == "paged":
+        assert counts["preempted"] > 0
+    assert ex.bm.num_free() == nb
