@@ -63,6 +63,7 @@ _CSRC = os.path.join(ROOT, "paged_kv_cache_400_amd", "csrc")
 TRAFFIC_SUMMARY = {
     "16": os.path.join(ROOT, "profiles", "pa_decode_streamk_mixed_step_traffic.md"),
     "fp8": os.path.join(ROOT, "profiles", "pa_decode_fp8_mixed_step_traffic.md"),
+    "prefill": os.path.join(ROOT, "profiles", "pa_prefill_chunked_prefill_traffic.md"),
 }
 KERNEL_SOURCES = {
     "16": [os.path.join(_CSRC, f) for f in ("decode_streamk.hip", "decode_streamk.h",
@@ -70,6 +71,8 @@ KERNEL_SOURCES = {
     "fp8": [os.path.join(_CSRC, f) for f in ("decode_fp8.hip", "decode_streamk.h",
                                              "pa_mfma_fp8.h", "pa_mfma.h", "pa_device.h",
                                              "pa_launch.h")],
+    "prefill": [os.path.join(_CSRC, f) for f in ("prefill.hip", "pa_mfma.h", "pa_device.h",
+                                                 "pa_launch.h")],
 }
 KERNEL_NAMES = {
     ("fp8", True): "pa_decode_fp8 (pa_decode_streamk over E4M3 pools + pa_streamk_reduce)",
@@ -293,6 +296,24 @@ def measure(b, dev, args, kv, partition_size, with_ceiling):
     return ms_step, ms_decode, ceiling
 
 
+def calibration_copy(mib):
+    """One device copy of a known size (a transfer to scale HBM byte
+    counters by): mib MiB read and mib MiB written."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    ms = c0.elapsed_time(c1)
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
+            "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def measure_prefill(b, dev, args):
     """K steps of the chunked-prefill step (append of the chunks' keys and
     values + pa_prefill) after W warmup steps; HIP events on the current
@@ -366,9 +387,15 @@ def prefill_line(args):
         "prefill_tokens_per_s": round(tq / (ms_step * 1e-3), 1),
         "roofline": {"kernel": "pa_prefill (pa_prefill_kernel)", "bound": "mfma",
                      "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "traffic_source": "not profiled"},
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
     }
+    traffic, note = measured_traffic("prefill")
+    if traffic is not None:
+        res["roofline"]["traffic"] = traffic
+        res["roofline"]["traffic_over_kv_bytes"] = round(traffic / b.kv_bytes(), 4)
+    res["roofline"]["traffic_source"] = note
+    if args.calibrate_copy_mib > 0:
+        res["calibration_copy"] = calibration_copy(args.calibrate_copy_mib)
     if args.cpu_baseline == "on":
         import oracle
         from paged_kv_cache_400_amd.workload import bits
@@ -526,20 +553,7 @@ def main():
         res["roofline"]["traffic_over_algorithmic"] = round(traffic / kv, 4)
     res["roofline"]["traffic_source"] = note if profiled else "not profiled"
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        dst.copy_(src)
-        c1.record()
-        torch.cuda.synchronize()
-        res["calibration_copy"] = {"bytes_read": n, "bytes_written": n,
-                                   "ms": round(c0.elapsed_time(c1), 5),
-                                   "gbs_read_plus_write": round(2 * n / (c0.elapsed_time(c1)
-                                                                         * 1e-3) / 1e9, 1)}
-        del src, dst
+        res["calibration_copy"] = calibration_copy(args.calibrate_copy_mib)
     if args.kv == "16" and args.fp8_summary == "on" and profiled:
         del dev
         b8 = wl.make_mixed_step(kv="fp8")
