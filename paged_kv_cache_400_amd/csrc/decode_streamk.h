@@ -226,7 +226,10 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     auto consume = [&](const uint4 (&kr)[KL], int buf, int t0) {
       if constexpr (kGather) {
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes);
-        gathered ^= kr[0].x ^ kr[KL - 1].w ^ vw[lane];
+        // every loaded K word enters the XOR, or the compiler narrows the loads
+#pragma unroll
+        for (int c = 0; c < KL; ++c) gathered ^= kr[c].x ^ kr[c].y ^ kr[c].z ^ kr[c].w;
+        gathered ^= vw[lane];
       } else {
         tw.consume(kr, buf, t0, p_end, qk_scale);
       }
