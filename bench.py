@@ -125,7 +125,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default 10; 50 with --mode prefill, whose "
+                         "matrix-core kernel runs below full clock for its first ~20 ms)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--ceiling", choices=["on", "off"], default="on",
                     help="also time pa_probe_gather (the same loads, no arithmetic)")
@@ -155,7 +157,10 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (a transfer of "
                          "known size to scale HBM byte counters by)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.warmup is None:
+        args.warmup = PREFILL_WARMUP if args.mode == "prefill" else 10
+    return args
 
 
 def cpu_baseline(b, seconds):
@@ -314,7 +319,13 @@ def calibration_copy(mib):
             "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
-def measure_prefill(b, dev, args):
+# Warmup steps of a chunked-prefill measurement: the GPU's clocks take about
+# 20 ms of matrix-core work to settle (per-dispatch durations fall by a
+# quarter over the first 20 steps, then stay flat).
+PREFILL_WARMUP = 50
+
+
+def measure_prefill(b, dev, args, warmup=None):
     """K steps of the chunked-prefill step (append of the chunks' keys and
     values + pa_prefill) after W warmup steps; HIP events on the current
     stream around the whole run and around each pa_prefill call.  Returns
@@ -332,7 +343,7 @@ def measure_prefill(b, dev, args):
         pa.prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                    dev["seq_lens"], qs, scale=b.scale, out=out)
 
-    for _ in range(args.warmup):
+    for _ in range(args.warmup if warmup is None else warmup):
         append()
         attend()
     torch.cuda.synchronize()
@@ -578,7 +589,7 @@ def main():
     if args.prefill_summary == "on" and profiled and args.kv == "16":
         pf = wl.make_chunked_prefill()
         devp = wl.to_device(pf, "cuda:0")
-        sp, ap = measure_prefill(pf, devp, args)
+        sp, ap = measure_prefill(pf, devp, args, warmup=max(args.warmup, PREFILL_WARMUP))
         fl = prefill_flops(pf.seq_lens, pf.query_start, pf.num_q_heads, pf.head_dim)
         res["chunked_prefill"] = {
             "workload": PREFILL_WORKLOAD + " (bench.py --mode prefill)",

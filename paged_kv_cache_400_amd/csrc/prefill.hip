@@ -13,25 +13,36 @@
 //
 // Row block: 16 query rows = 16 / G consecutive chunk tokens x the G query
 // heads of one KV head, so the q.K^T MFMA (16 positions x 16 rows) has no
-// idle rows.  Work unit: one wave per (sequence, KV head, kNrb = 3
-// consecutive row blocks).  The wave walks the sequence's tiles of 16
-// positions from 0 up to its last row's position with TileWave (pa_mfma.h):
-// K to registers and V to LDS once per tile, each tile issued one tile
-// ahead, consumed by the three row blocks' tile waves; each lane's row has
-// its own causal end, which masks its scores.  No split and no merge: a
-// chunk has many units per (sequence, head).
+// idle rows.  Work unit: one workgroup of 4 waves per (sequence, KV head,
+// 4 x kNrb consecutive row blocks); each wave owns kNrb = 3 row blocks.
+// The workgroup walks the sequence's positions from 0 up to its last row's
+// position in tiles of 32, double-buffered in LDS: after a wait and a
+// barrier, the four waves copy the next tile's keys and values from HBM
+// straight into LDS (global_load_lds) while they compute the current one,
+// so each key and value is fetched once per unit, not once per wave.
+//
+// Per wave and 32-position slab: q.K^T as two 16-position halves (K read
+// from LDS in the MFMA operand layout); the softmax on the 8 scores a lane
+// holds per row, masked only where the slab reaches past the wave's first
+// token; P.V as v_mfma_f32_16x16x32 (the lane's 8 weights, positions
+// 4 grp + r then 16 + 4 grp + r, are its k-values, and the V operand is the
+// two halves' transpose reads side by side), which runs at twice the rate
+// of the 16x16x16 form on gfx950; the denominator as one more MFMA of the
+// weights against a column of ones, so it accumulates in the rows' own
+// layout (no lane exchange at the end).  No split and no merge.
 //
 // Placement: workgroup g runs on XCD g % 8; pair (s, kh) belongs to XCD
-// (s * hkv + kh) % 8, whose waves take its units consecutively (the last,
-// longest ones first), so the units of a pair share one L2 for the pair's
-// keys and values.
+// (s * hkv + kh) % 8, whose workgroups take its units consecutively (the
+// last, longest ones first), so the units of a pair share one L2.
 //
 // Roofline: the useful work is 4 d FLOPs per (query row, visible
-// position); the kernel is bound by on-chip work (matrix cores, the softmax,
-// the per-tile loads from L2), not by HBM.  Measured on the 32 x 512-token
-// chunked-prefill step: one row block per unit, units in plain order
-// 5.39 ms; units grouped per XCD 3.99 ms; two row blocks per unit (2 waves
-// per SIMD) 1.86 ms; three 1.55 ms (four, at one wave per SIMD, 3.27 ms).
+// position); the kernel is bound by on-chip work (matrix cores, the softmax
+// and the LDS traffic), not by HBM.  Measured on the 32 x 512-token
+// chunked-prefill step: one wave per unit, each loading its own tiles,
+// 1.52 ms; tiles shared by the workgroup through LDS 1.25 ms; 32-position
+// tiles and the 16x16x32 P.V form 1.02 ms; the mask only on the diagonal,
+// the scale folded into one FMA per weight and the denominator on the
+// matrix cores 0.93 ms.
 #include "pa_launch.h"
 #include "pa_mfma.h"
 
@@ -41,8 +52,88 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 16;  // query rows per row block
-constexpr int kNrb = 3;    // row blocks per unit
+constexpr int kRows = 16;          // query rows per row block
+constexpr int kNrb = 3;            // row blocks per wave
+constexpr int kSub = 2;            // 16-position sub-tiles per tile
+constexpr int kTP = kTile * kSub;  // positions per tile
+
+// LDS of one tile (one stage of the double buffer): the K operand blocks,
+// then the V sub-tiles.  K block (sub-tile st, d-chunk c) holds, at byte
+// 16 l, the 16 bytes lane l feeds the q.K^T MFMA: position 16 st + l % 16,
+// elements 32 c + 8 (l / 16) .. + 7, so a wave reads it back linearly.  V
+// sub-tiles use the transpose-read layout of Geo<D>.
+template <int D>
+struct Stage {
+  using GE = Geo<D>;
+  static constexpr int KBLK = 64 * 16;
+  static constexpr int KSUB = GE::KC * KBLK;
+  static constexpr int KBYTES = kSub * KSUB;
+  static constexpr int BYTES = KBYTES + kSub * GE::TILE;
+  static constexpr int KJOBS = kSub * GE::KC;  // DMA instructions per tile: K blocks,
+  static constexpr int JOBS = KJOBS + kSub * 4;  // then V regions
+  static_assert(JOBS % kWaves == 0, "every wave issues the same number of copies");
+  static_assert(kSub % 2 == 0, "whole 32-position slabs");
+  static_assert(BYTES % 32 == 0, "stages and the per-wave staging stay 16-byte aligned");
+};
+
+// The V operands of one 32-position slab: for each column block m, the
+// transpose reads (ds_read_b64_tr_b16) at lo_base + 32 m (first sub-tile)
+// and hi_base + 32 m (second), completed before the block ends.  One asm
+// block: the compiler would otherwise make these reads wait for every LDS
+// copy in flight, the next tile's included.  The caller's wait and barrier
+// order them after the copies of this tile.
+template <int NM>
+__device__ __forceinline__ void read_v_slab(uint2 (&lo)[NM], uint2 (&hi)[NM],
+                                            const unsigned char* lo_base,
+                                            const unsigned char* hi_base) {
+  const uint32_t a = (uint32_t)(uintptr_t)lo_base;
+  const uint32_t b = (uint32_t)(uintptr_t)hi_base;
+  static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
+  if constexpr (NM == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:32\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:32\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:64\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:96\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:96\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:128\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:160\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:160\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:192\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:224\n\t"
+        "ds_read_b64_tr_b16 %15, %17 offset:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+          "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
+        : "v"(a), "v"(b)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:32\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:64\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+          "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(a), "v"(b)
+        : "memory");
+  }
+}
+
+// Two 16-bit ones packed in a word (the B operand of a row sum).
+template <typename T> constexpr uint32_t kOnes2 = 0x3c003c00u;  // fp16 1.0
+template <> constexpr uint32_t kOnes2<BF16> = 0x3f803f80u;      // bf16 1.0
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 #pragma unroll
@@ -63,11 +154,17 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                   const int32_t* __restrict__ query_start, int32_t num_seqs, int32_t total_q,
                   int32_t hkv, int32_t mb, int32_t nb, float qk_scale) {
   using GE = Geo<D>;
+  using SG = Stage<D>;
   constexpr int KC = GE::KC, NM = GE::NM;
   constexpr int R1 = kRows / G;   // chunk tokens per row block
-  constexpr int R = kNrb * R1;     // chunk tokens per unit
-  static_assert(kRows % G == 0, "whole tokens per unit");
-  __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * GE::TILE];
+  constexpr int R = kNrb * R1;     // chunk tokens per wave
+  constexpr int RW = kWaves * R;   // chunk tokens per workgroup
+  static_assert(kRows % G == 0, "whole tokens per row block");
+  __shared__ __attribute__((aligned(16))) unsigned char s_st0[SG::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_st1[SG::BYTES];
+  unsigned char* const s_mem = s_st0;
+  static_assert(sizeof(float) * kRows * D <= 2 * SG::BYTES / kWaves,
+                "a row block's result fits the wave's quarter of the LDS");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,14 +178,14 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     n = (qs >= 0 && qe >= qs && qe <= total_q) ? qe - qs : 0;
   };
 
-  // ---- this wave's (sequence, KV head, unit).  Workgroup g runs on XCD
-  // g % 8; pair p = s * hkv + kh belongs to XCD p % 8, and an XCD's waves
-  // take its pairs in order, a pair's units consecutively, so the units of
-  // one pair share that XCD's L2 for the pair's keys and values.
+  // ---- this workgroup's (sequence, KV head, unit).  Workgroup g runs on
+  // XCD g % 8; pair p = s * hkv + kh belongs to XCD p % 8, and an XCD's
+  // workgroups take its pairs in order, a pair's units consecutively, so the
+  // units of one pair share that XCD's L2.
   const int xcd = blockIdx.x % 8;
-  const int un = (blockIdx.x / 8) * kWaves + w;  // unit index within the XCD
+  const int un = blockIdx.x / 8;  // unit index within the XCD
   const int npairs = num_seqs * hkv;
-  int s = -1, kh = 0, rb_local = 0;
+  int s = -1, kh = 0, u_local = 0;
   {
     int run = 0;
     for (int j0 = 0; xcd + 8 * j0 < npairs; j0 += 64) {
@@ -97,7 +194,7 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       if (p < npairs) {
         int qs_, n_;
         chunk_of(p / hkv, qs_, n_);
-        cnt = (n_ + R - 1) / R;
+        cnt = (n_ + RW - 1) / RW;
       }
       const int incl = wave_inclusive_scan(cnt, lane);
       const uint64_t hit = __builtin_amdgcn_ballot_w64(run + incl > un);
@@ -106,35 +203,39 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         const int pp = xcd + 8 * (j0 + i);
         s = pp / hkv;
         kh = pp % hkv;
-        rb_local = un - (run + __builtin_amdgcn_readlane(incl, i) -
-                         __builtin_amdgcn_readlane(cnt, i));
+        u_local = un - (run + __builtin_amdgcn_readlane(incl, i) -
+                        __builtin_amdgcn_readlane(cnt, i));
         break;
       }
       run += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  if (s < 0) return;  // past the last unit
+  if (s < 0) return;  // past the last unit (the same for every wave)
   int qs, n;
   chunk_of(s, qs, n);
   const int L = seq_lens[s];
-  const int nrb = (n + R - 1) / R;    // units of this pair
-  const int rb = nrb - 1 - rb_local;  // last units first: they see the most positions
-  const int i0 = rb * R;              // first chunk token of this unit
+  const int nu = (n + RW - 1) / RW;  // units of this pair
+  const int i0 = (nu - 1 - u_local) * RW;  // last units first: they see the most positions
+  const int iw = i0 + w * R;               // this wave's first chunk token
   const int col = lane & 15, grp = lane >> 4;
   const bool valid = n <= L && (int64_t)L <= max_len;
-  // the lane's query row in row block h (h < kNrb): chunk token i0 + h R1 +
-  // col / G, head kh * G + col % G; its causal end (exclusive)
+  const bool wave_on = iw < n;
+  // the lane's query row in row block h: chunk token iw + h R1 + col / G,
+  // head kh * G + col % G; its causal end (exclusive)
   int tok[kNrb], lane_end[kNrb];
   bool active[kNrb];
 #pragma unroll
   for (int h = 0; h < kNrb; ++h) {
-    tok[h] = i0 + h * R1 + col / G;
+    tok[h] = iw + h * R1 + col / G;
     active[h] = tok[h] < n;
     lane_end[h] = active[h] ? L - n + tok[h] + 1 : 1;
   }
-  const int p_end = L - n + min(i0 + R, n);
-  auto store_rows = [&](const float* st, int tfirst) {
-    // st: [16 rows][D] floats staged in LDS; row r -> (token tfirst + r / G, head r % G)
+  const int wave_end = L - n + min(iw + R, n);  // positions this wave needs
+  const int p_end = L - n + min(i0 + RW, n);    // positions the workgroup loads
+
+  float* st = reinterpret_cast<float*>(s_mem + w * (2 * SG::BYTES / kWaves));  // [16][D]
+  auto store_rows = [&](int tfirst) {
+    // st: 16 rows staged in LDS; row r -> (token tfirst + r / G, head r % G)
     for (int i = lane * 8; i < kRows * D; i += 64 * 8) {
       const int r = i / D, d = i % D;
       const int t_r = tfirst + r / G;
@@ -148,33 +249,45 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
   };
 
-  unsigned char* vtile = s_mem + w * 2 * GE::TILE;
-  float* st = reinterpret_cast<float*>(vtile);  // [16][D] staging once the tiles are consumed
-  static_assert(sizeof(float) * kRows * D <= 2 * GE::TILE, "the result fits the wave's V tiles");
-
   if (!valid) {  // lengths break the contract: NaN rows, nothing read
+    if (!wave_on) return;
     for (int i = lane; i < kRows * D; i += 64) st[i] = __builtin_nanf("");
 #pragma unroll
-    for (int h = 0; h < kNrb; ++h) store_rows(st, i0 + h * R1);
+    for (int h = 0; h < kNrb; ++h) store_rows(iw + h * R1);
     return;
   }
 
-  TileWave<T, D, BS, kRows> tws[kNrb];
+  // per row block: q operand, P.V accumulators, running max (scaled, base
+  // 2) and the denominator, accumulated by the matrix cores as P times a
+  // column of ones, so it lands in the accumulators' row layout.  A
+  // negative scale is moved into q (exact sign flips), so the running max
+  // can be taken on the raw scores.
+  const uint32_t q_sign = qk_scale < 0.0f ? 0x80008000u : 0u;
+  const float sc_scale = fabsf(qk_scale);
+  uint4 qb[kNrb][KC];
+  f32x4_t acc[kNrb][NM], lacc[kNrb];
+  float m_run[kNrb];
 #pragma unroll
   for (int h = 0; h < kNrb; ++h) {
-    tws[h].init(kc, vc, hkv, kh, vtile);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      tws[h].qb[c] = make_uint4(0u, 0u, 0u, 0u);
-      if (active[h])
-        tws[h].qb[c] = *reinterpret_cast<const uint4*>(
+      qb[h][c] = make_uint4(0u, 0u, 0u, 0u);
+      if (active[h]) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
             q + (((int64_t)qs + tok[h]) * hq + kh * G + col % G) * D + (c * 4 + grp) * 8);
+        qb[h][c] = make_uint4(v.x ^ q_sign, v.y ^ q_sign, v.z ^ q_sign, v.w ^ q_sign);
+      }
     }
-    tws[h].reset();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[h][m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    lacc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[h] = kNegInf;
   }
-  auto& tw = tws[0];  // issues the loads every row block consumes
+  const uint4 ones = make_uint4(kOnes2<T>, kOnes2<T>, kOnes2<T>, kOnes2<T>);
+  // positions every stored row of the wave sees (its first token's end)
+  const int wave_min_end = L - n + iw + 1;
 
-  // block ids of the positions [0, p_end), 64 at a time: lane j holds block base + j
+  // block ids of the positions [0, p_end), 64 at a time: lane j holds block blk_base + j
   const int32_t* bt_row = block_tables + (int64_t)s * mb;
   const int blk_last = (p_end - 1) / BS;
   int blk_base = 0;
@@ -192,68 +305,165 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     return id;
   };
   int vid = load_ids();
-  const int ntiles = (p_end + kTile - 1) / kTile;
+  const int ntiles = (p_end + kTP - 1) / kTP;
+  const int64_t blk_stride = (int64_t)hkv * BS * D;
+  const uint16_t* kh_k = kc + (int64_t)kh * BS * D;
+  const uint16_t* kh_v = vc + (int64_t)kh * BS * D;
 
-  auto issue = [&](uint4 (&kr)[KC], int buf, int j) {
-    const int t0 = j * kTile;
-    int b = t0 / BS - blk_base;
-    if (b + TileWave<T, D, BS, kRows>::kIds - 1 >= 64) {
-      blk_base += b;
-      b = 0;
+  // The workgroup's copies of tile j (positions clamped to p_end - 1) into
+  // stage sg, straight from HBM to LDS; wave w issues copies w, w + 4, ...
+  auto issue = [&](int j, unsigned char* stage) {
+    const int t0 = j * kTP;
+    if ((min(t0 + kTP, p_end) - 1) / BS - blk_base >= 64) {
+      blk_base = t0 / BS;
       vid = load_ids();
     }
-    const int id0 = __builtin_amdgcn_readlane(vid, b);
-    int id1 = id0;
-    if constexpr (BS < kTile) id1 = (t0 + BS < p_end) ? __builtin_amdgcn_readlane(vid, b + 1) : id0;
-    tw.issue(kr, buf, t0, p_end - 1, id0, id1);
-  };
-
-  uint4 ka[KC], kb[KC];
-  issue(ka, 0, 0);
-  for (int j = 0;;) {
-    wait_vmem_all();
-    if (j + 1 < ntiles) issue(kb, 1, j + 1);
 #pragma unroll
-    for (int h = 0; h < kNrb; ++h) tws[h].consume(ka, 0, j * kTile, lane_end[h], qk_scale);
-    if (++j >= ntiles) break;
-    wait_vmem_all();
-    if (j + 1 < ntiles) issue(ka, 0, j + 1);
-#pragma unroll
-    for (int h = 0; h < kNrb; ++h) tws[h].consume(kb, 1, j * kTile, lane_end[h], qk_scale);
-    if (++j >= ntiles) break;
-  }
-#pragma unroll
-  for (int h = 0; h < kNrb; ++h) tws[h].finish();
-
-  // out = acc / l, staged row-major in the wave's V tiles, stored whole lines
-  auto put = [&](const TileWave<T, D, BS, kRows>& t) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * grp + r;
-      const float l_h = __shfl(t.l_run, h);
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : t.acc[m][r] / l_h;
+    for (int k = 0; k < SG::JOBS / kWaves; ++k) {
+      const int job = k * kWaves + w;
+      if (job < SG::KJOBS) {
+        const int sb = job / KC, c = job % KC;
+        const int t = min(t0 + kTile * sb + col, p_end - 1);
+        const int id = __shfl(vid, t / BS - blk_base);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kh_k + id * blk_stride + (t % BS) * D + 32 * c + 8 * grp),
+            (void __attribute__((address_space(3)))*)(stage + job * SG::KBLK), 16, 0,
+            kCachePolicyStream);
+      } else {
+        const int vj = job - SG::KJOBS, sb = vj / 4, i = vj % 4;
+        const int t = min(t0 + kTile * sb + 4 * i + lane / (D / 8), p_end - 1);
+        const int id = __shfl(vid, t / BS - blk_base);
+        if (GE::LANES == 64 || lane < GE::LANES)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(kh_v + id * blk_stride + (t % BS) * D + (lane % (D / 8)) * 8),
+              (void __attribute__((address_space(3)))*)(stage + SG::KBYTES + sb * GE::TILE +
+                                                        i * GE::REGION),
+              16, 0, kCachePolicyStream);
+      }
     }
   };
+
+  // The wave's row blocks over tile j, in slabs of 32 positions (two
+  // sub-tiles): slabs past the wave's last position are skipped; each lane
+  // masks at its own row's end.  q.K^T per sub-tile gives lane (col, grp)
+  // the scores of positions 4 grp + r (first sub-tile) and 16 + 4 grp + r
+  // (second); these 8 weights, in that order, are the lane's k-values of
+  // the 16x16x32 P.V product, whose V operand is therefore the two
+  // sub-tiles' transpose reads side by side.
+  auto compute = [&](int j, const unsigned char* stage) {
+#pragma unroll 1
+    for (int sl = 0; sl < kSub / 2; ++sl) {
+      const int t0 = j * kTP + 2 * kTile * sl;
+      if (t0 >= wave_end) break;
+      uint4 k0[KC], k1[KC];
+      const unsigned char* kb = stage + 2 * sl * KC * SG::KBLK + 16 * lane;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        k0[c] = *reinterpret_cast<const uint4*>(kb + c * SG::KBLK);
+        k1[c] = *reinterpret_cast<const uint4*>(kb + (KC + c) * SG::KBLK);
+      }
+      uint4 pa_op[kNrb];
+#pragma unroll
+      for (int h = 0; h < kNrb; ++h) {
+        f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) s0 = mfma_k32<T>(k0[c], qb[h][c], s0);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) s1 = mfma_k32<T>(k1[c], qb[h][c], s1);
+        // only slabs that reach past the first token's end need the mask;
+        // rows of tokens past the chunk are never stored
+        if (t0 + 2 * kTile > wave_min_end) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (t0 + 4 * grp + r >= lane_end[h]) s0[r] = kNegInf;
+            if (t0 + kTile + 4 * grp + r >= lane_end[h]) s1[r] = kNegInf;
+          }
+        }
+        const float lm =
+            fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                  fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * sc_scale;
+        if (__builtin_amdgcn_ballot_w64(lm > m_run[h] + kRescaleSlack) != 0) {
+          float mx = fmaxf(lm, __shfl_xor(lm, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run[h], mx);
+          const float corr = exp2_fast(m_run[h] - m_new);  // 0 when m_run = -inf
+          m_run[h] = m_new;
+          float cr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            lacc[h][r] *= cr[r];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[h][m][r] *= cr[r];
+          }
+        }
+        // weight = 2^(score * scale - m), one FMA and one exp each
+        const float nm = -m_run[h];
+        pa_op[h] = make_uint4(
+            pack2<T>(exp2_fast(fmaf(s0[0], sc_scale, nm)), exp2_fast(fmaf(s0[1], sc_scale, nm))),
+            pack2<T>(exp2_fast(fmaf(s0[2], sc_scale, nm)), exp2_fast(fmaf(s0[3], sc_scale, nm))),
+            pack2<T>(exp2_fast(fmaf(s1[0], sc_scale, nm)), exp2_fast(fmaf(s1[1], sc_scale, nm))),
+            pack2<T>(exp2_fast(fmaf(s1[2], sc_scale, nm)), exp2_fast(fmaf(s1[3], sc_scale, nm))));
+        lacc[h] = mfma_k32<T>(pa_op[h], ones, lacc[h]);
+      }
+      // V operand of column block m: rows 4 grp + r of the first sub-tile,
+      // then of the second, column 16 m + col
+      const unsigned char* vb = stage + SG::KBYTES + 2 * sl * GE::TILE + grp * GE::REGION +
+                                (col >> 2) * GE::ROW + 8 * (col & 3);
+      uint2 vlo[NM], vhi[NM];
+      read_v_slab<NM>(vlo, vhi, vb, vb + GE::TILE);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint4 vop = make_uint4(vlo[m].x, vlo[m].y, vhi[m].x, vhi[m].y);
+#pragma unroll
+        for (int h = 0; h < kNrb; ++h) acc[h][m] = mfma_k32<T>(pa_op[h], vop, acc[h][m]);
+      }
+    }
+  };
+
+  // one tile in flight while the previous one is computed; one barrier a tile
+  issue(0, s_st0);
+  for (int j = 0;;) {
+    wait_vmem_all();
+    __syncthreads();  // tile j is in LDS; every wave is done with tile j - 1
+    if (j + 1 < ntiles) issue(j + 1, s_st1);
+    if (wave_on) compute(j, s_st0);
+    if (++j >= ntiles) break;
+    wait_vmem_all();
+    __syncthreads();
+    if (j + 1 < ntiles) issue(j + 1, s_st0);
+    if (wave_on) compute(j, s_st1);
+    if (++j >= ntiles) break;
+  }
+  __syncthreads();  // the stages are free: each wave stages its rows in its quarter
+  if (!wave_on) return;
+
+  // out = acc / l, staged row-major, stored whole lines
 #pragma unroll
   for (int h = 0; h < kNrb; ++h) {
-    put(tws[h]);
-    store_rows(st, i0 + h * R1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * grp + r;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        st[row * D + 16 * m + col] = bad ? __builtin_nanf("") : acc[h][m][r] / lacc[h][r];
+    }
+    store_rows(iw + h * R1);
   }
 }
 
-// Units one XCD can get at most: each sequence has at most ceil(hkv / 8)
-// of its (sequence, KV head) pairs on one XCD.
+// Units (workgroups) one XCD can get at most: each sequence has at most
+// ceil(hkv / 8) of its (sequence, KV head) pairs on one XCD, and a pair's
+// chunk of n tokens has ceil(n / tokens per unit) units.
 static int64_t units_per_xcd(int32_t total_q, int32_t num_seqs, int32_t hkv, int32_t group) {
-  return ((int64_t)hkv + 7) / 8 *
-         (((int64_t)total_q * group + kNrb * kRows - 1) / (kNrb * kRows) + num_seqs);
+  const int64_t per_unit = kWaves * kNrb * kRows / group;
+  return ((int64_t)hkv + 7) / 8 * (((int64_t)total_q + per_unit - 1) / per_unit + num_seqs);
 }
 
 template <typename T, int D, int BS, int G>
 static hipError_t launch_t(const PrefillArgs& a) {
-  const int64_t per_xcd = units_per_xcd(a.total_q, a.num_seqs, a.num_kv_heads, G);
-  const int64_t grid = 8 * ((per_xcd + kWaves - 1) / kWaves);
+  const int64_t grid = 8 * units_per_xcd(a.total_q, a.num_seqs, a.num_kv_heads, G);
   hipLaunchKernelGGL((pa_prefill_kernel<T, D, BS, G>), dim3((uint32_t)grid), dim3(kThreads), 0,
                      a.stream, (uint16_t*)a.out, (const uint16_t*)a.q,
                      (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
@@ -297,7 +507,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
 }
 
 int64_t prefill_units(int32_t total_q, int32_t num_seqs, int32_t num_kv_heads, int32_t group) {
-  return 8 * kWaves * ((units_per_xcd(total_q, num_seqs, num_kv_heads, group) + kWaves - 1) / kWaves);
+  return 8 * kWaves * units_per_xcd(total_q, num_seqs, num_kv_heads, group);
 }
 
 }  // namespace pa
