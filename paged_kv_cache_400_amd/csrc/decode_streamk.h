@@ -9,25 +9,30 @@
 // PagedAttention solve ...", section "How PagedAttention works").  What
 // differs is how the work is cut.
 //
-// Global tile order: the (sequence, KV head) pairs back to back, pair
-// s * hkv + kh holding ceil(L_s / n) tiles of n positions (n = 16 for
-// 16-bit pools, 32 for 8-bit ones).  The launch has
-// exactly as many waves as the GPU keeps resident, and wave w takes the
-// contiguous run of tiles [w C, (w + 1) C) with C = ceil(total / waves)
-// (at least kMinChunk).  Every wave therefore streams the same number of
-// tiles (to one tile), never waits for another wave, and never sits idle at
-// the end of a work unit: the partitioned kernels spend a merge through LDS
-// and a barrier on every (sequence, head, 512-position) unit, and their
-// units differ in size.  Each wave finds its first pair from a prefix sum of
-// the tile counts (recomputed by every wave from seq_lens; a few hundred
-// integers from L2), then walks its run pair by pair:
+// Tile order: for each KV head, the sequences' tiles back to back, sequence
+// s holding ceil(L_s / n) tiles of n positions (n = 16 for 16-bit pools, 32
+// for 8-bit ones).  The launch has as many waves as the GPU keeps resident
+// (a whole number per KV head); wave w works on head w % hkv and takes the
+// (w / hkv)-th of that head's equal runs of C = ceil(tiles per head / waves
+// per head) tiles (at least kMinChunk).  Adjacent waves therefore read the
+// same positions of adjacent heads, neighbouring pieces of the same pool
+// blocks, at about the same time: 2% faster on the mixed decode step than
+// the pairs in (sequence, head) order, 4% with 8-bit pools.  Every wave
+// streams the same number of tiles (to one tile), never waits for another
+// wave, and never sits idle at the end of a work unit: the partitioned
+// kernels spend a merge through LDS and a barrier on every (sequence, head,
+// 512-position) unit, and their units differ in size.  Each wave finds its
+// first sequence from a prefix sum of the tile counts (recomputed by every
+// wave from seq_lens; a few hundred integers from L2), then walks its run
+// sequence by sequence:
 //   - a pair that lies wholly inside the run is finished in place: out =
 //     acc / l, rounded to the output type;
 //   - a pair cut by the run's start or end leaves a partial (m, l, acc) in
 //     the wave's slot 0 (the pair it starts in) or slot 1 (the pair it ends
 //     in) of the workspace;
-//   - the wave that processes a pair's last tile records which waves hold
-//     its partials (meta), and pa_streamk_reduce merges them by log-sum-exp
+//   - the wave that processes a pair's last tile records which runs of the
+//     head hold its partials (meta; run c of head kh is wave c * hkv + kh),
+//     and pa_streamk_reduce merges them by log-sum-exp
 //     ("Continuous Batching & Paged Attention", section "Attention needs
 //     memory that grows with the conversation": plain softmax attention; the
 //     merge is the identity M = max m_p, out = sum 2^(m_p - M) acc_p /
@@ -118,25 +123,31 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     return (L > 0 && (int64_t)L <= max_len) ? (L + kT - 1) / kT : 0;
   };
 
-  // ---- this wave's run of the global tile order
+  // ---- this wave's run: wave w works on KV head w % hkv, and the waves of
+  // one head split that head's tile order (the sequences' tiles back to
+  // back) into equal runs.  Adjacent waves take adjacent heads of the same
+  // positions, so they read neighbouring pieces of the same pool blocks at
+  // about the same time.
+  const int nwh = nwaves / hkv;  // waves per head (the launch has nwaves >= hkv)
+  const int kh0 = wave % hkv, jw = wave / hkv;
+  if (jw >= nwh) return;
   int64_t per_head = 0;  // sum over sequences of their tile counts
   for (int b = 0; b < num_seqs; b += 64) {
     const int n = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) : 0;
     per_head += wave_sum(n);
   }
-  const int64_t total = per_head * hkv;
-  const int64_t chunk = max((int64_t)kMinChunk, (total + nwaves - 1) / nwaves);
-  const int64_t g0 = (int64_t)wave * chunk;
-  if (g0 >= total) return;
-  const int64_t g1 = min(total, g0 + chunk);
+  const int64_t chunk = max((int64_t)kMinChunk, (per_head + nwh - 1) / nwh);
+  const int64_t g0 = (int64_t)jw * chunk;
+  if (g0 >= per_head) return;
+  const int64_t g1 = min(per_head, g0 + chunk);
 
-  // first sequence whose tiles reach past g0, and where its pairs start
+  // first sequence whose tiles reach past g0, and where its tiles start
   int s = -1;
-  int64_t seq_start = 0;  // global index of the sequence's first tile
+  int64_t seq_start = 0;  // index of the sequence's first tile in the head's order
   {
     int64_t run = 0;
     for (int b = 0; b < num_seqs; b += 64) {
-      const int span = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) * hkv : 0;
+      const int span = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) : 0;
       const int incl = wave_inclusive_scan(span, lane);
       const uint64_t hit = __builtin_amdgcn_ballot_w64(run + incl > g0);
       if (hit != 0) {
@@ -148,12 +159,12 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       run += lane_value(incl, 63);
     }
   }
-  if (s < 0) return;  // unreachable: g0 < total
+  if (s < 0) return;  // unreachable: g0 < per_head
   int L = seq_lens[s];
   int ns = tiles_of(L);
   if (ns == 0) return;  // unreachable: the first hit has tiles
-  int kh = (int)((g0 - seq_start) / ns);
-  int t_lo = (int)((g0 - seq_start) % ns);
+  const int kh = kh0;
+  int t_lo = (int)(g0 - seq_start);
 
   // The segment's result: final rows for a pair wholly inside the run, else
   // a partial in slot 0 (the run's first pair) or 1 (its last); the wave
@@ -290,16 +301,13 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 
     g += ntiles;
     if (g >= g1) break;
-    // the run goes on, so this pair ended here: next pair
+    // the run goes on, so this sequence ended here: the next one, same head
     t_lo = 0;
-    if (++kh == hkv) {
-      kh = 0;
-      do {
-        if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
-        L = seq_lens[s];
-        ns = tiles_of(L);
-      } while (ns == 0);
-    }
+    do {
+      if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
+      L = seq_lens[s];
+      ns = tiles_of(L);
+    } while (ns == 0);
   }
 }
 
@@ -340,7 +348,7 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
         ml[u] = make_float2(kNegInf, 0.0f);
         a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (c <= c_last) {
-          const int64_t slot = 2 * (int64_t)c + (c == c_first ? meta.z : 0);
+          const int64_t slot = 2 * ((int64_t)c * hkv + kh) + (c == c_first ? meta.z : 0);
           ml[u] = ws_ml[slot * G + h];
           a[u] = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
         }
@@ -398,16 +406,20 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
   int waves = resident_waves<T, KV, D, BS, G>();
   if (waves <= 0) return hipErrorInvalidDevice;
-  waves = min(waves, kStreamKMaxWaves) / kWaves * kWaves;
+  if (a.num_kv_heads > kStreamKMaxWaves) return hipErrorInvalidValue;
+  // a whole number of waves per KV head, at least one
+  waves = max(min(waves, kStreamKMaxWaves) / a.num_kv_heads, 1) * a.num_kv_heads;
   if (gather) {  // the same grid, gather-only (the group does not change the loads)
-    hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, 1, true, KV>), dim3((uint32_t)(waves / kWaves)),
+    hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, 1, true, KV>),
+                       dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
                        dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
                        nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                        a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
                        a.max_blocks_per_seq, a.num_blocks, waves, 0.0f, 0.0f);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>), dim3((uint32_t)(waves / kWaves)),
+  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>),
+                     dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
                      (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                      a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
