@@ -35,6 +35,12 @@
 // (s * hkv + kh) % 8, whose workgroups take its units consecutively (the
 // last, longest ones first), so the units of a pair share one L2.
 //
+// Copies: each lane's byte offset within a pool block is fixed per copy, so
+// a tile that lies wholly below the unit's last position costs a readlane of
+// its block id, a scalar multiply and one add per copy; only the unit's last
+// tile clamps rows one by one.  V sub-tiles are stored with a chunk swizzle
+// (VGeo below) that halves the bank conflicts of the transpose reads.
+//
 // Roofline: the useful work is 4 d FLOPs per (query row, visible
 // position); the kernel is bound by on-chip work (matrix cores, the softmax
 // and the LDS traffic), not by HBM.  Measured on the 32 x 512-token
@@ -42,7 +48,8 @@
 // 1.52 ms; tiles shared by the workgroup through LDS 1.25 ms; 32-position
 // tiles and the 16x16x32 P.V form 1.02 ms; the mask only on the diagonal,
 // the scale folded into one FMA per weight and the denominator on the
-// matrix cores 0.93 ms.
+// matrix cores 0.93 ms; scalar block addressing for whole tiles and the
+// swizzled V layout 0.86 ms.
 #include "pa_launch.h"
 #include "pa_mfma.h"
 
@@ -57,18 +64,40 @@ constexpr int kNrb = 3;            // row blocks per wave
 constexpr int kSub = 2;            // 16-position sub-tiles per tile
 constexpr int kTP = kTile * kSub;  // positions per tile
 
+// LDS layout of the V sub-tiles (16 rows each): four regions of 4 rows,
+// regions 128 bytes apart modulo the 256-byte bank period, and within a
+// region the 16-byte chunks of row r stored at chunk index c ^ (2 sw(r)).
+// A transpose read (ds_read_b64_tr_b16) of column block m gives each group
+// of 16 lanes 32 bytes of each of its region's 4 rows: with the swizzle the
+// 4 rows fall on distinct banks, and the 4 groups pair up on the two halves
+// of the bank period, so an instruction meets each bank twice (the least
+// for its 512 bytes) instead of four times.
+template <int D>
+struct VGeo {
+  static constexpr int ROW = 2 * D;             // bytes of one V row
+  static constexpr int CHUNKS = D / 8;          // 16-byte chunks per row
+  static constexpr int REGION = 4 * ROW + 128;  // 4 rows + padding
+  static constexpr int TILE = 4 * REGION;       // one 16-row sub-tile
+  static constexpr int LANES = 4 * CHUNKS;      // lanes that fill a region
+  static constexpr int SWDIV = 256 / ROW;       // rows per bank period
+  static_assert(TILE % 32 == 0 && (REGION % 256) == 128, "bank layout");
+};
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return r / VGeo<D>::SWDIV;
+}
+
 // LDS of one tile (one stage of the double buffer): the K operand blocks,
 // then the V sub-tiles.  K block (sub-tile st, d-chunk c) holds, at byte
 // 16 l, the 16 bytes lane l feeds the q.K^T MFMA: position 16 st + l % 16,
-// elements 32 c + 8 (l / 16) .. + 7, so a wave reads it back linearly.  V
-// sub-tiles use the transpose-read layout of Geo<D>.
+// elements 32 c + 8 (l / 16) .. + 7, so a wave reads it back linearly.
 template <int D>
 struct Stage {
   using GE = Geo<D>;
   static constexpr int KBLK = 64 * 16;
   static constexpr int KSUB = GE::KC * KBLK;
   static constexpr int KBYTES = kSub * KSUB;
-  static constexpr int BYTES = KBYTES + kSub * GE::TILE;
+  static constexpr int BYTES = KBYTES + kSub * VGeo<D>::TILE;
   static constexpr int KJOBS = kSub * GE::KC;  // DMA instructions per tile: K blocks,
   static constexpr int JOBS = KJOBS + kSub * 4;  // then V regions
   static_assert(JOBS % kWaves == 0, "every wave issues the same number of copies");
@@ -77,56 +106,57 @@ struct Stage {
 };
 
 // The V operands of one 32-position slab: for each column block m, the
-// transpose reads (ds_read_b64_tr_b16) at lo_base + 32 m (first sub-tile)
-// and hi_base + 32 m (second), completed before the block ends.  One asm
-// block: the compiler would otherwise make these reads wait for every LDS
-// copy in flight, the next tile's included.  The caller's wait and barrier
-// order them after the copies of this tile.
+// transpose reads of the first sub-tile (lo) and of the second (hi, one
+// VGeo tile further).  a[i] is the lane's address of column block i ^ sw
+// in the first sub-tile (i < 4); block m is at a[m & 3] + 128 (m >> 2).
+// One asm block, completed before it ends: the compiler would otherwise
+// make these reads wait for every LDS copy in flight, the next tile's
+// included.  The caller's wait and barrier order them after the copies of
+// this tile.
 template <int NM>
 __device__ __forceinline__ void read_v_slab(uint2 (&lo)[NM], uint2 (&hi)[NM],
-                                            const unsigned char* lo_base,
-                                            const unsigned char* hi_base) {
-  const uint32_t a = (uint32_t)(uintptr_t)lo_base;
-  const uint32_t b = (uint32_t)(uintptr_t)hi_base;
+                                            const uint32_t (&a)[4]) {
   static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
   if constexpr (NM == 8) {
+    static_assert(VGeo<128>::TILE == 4608, "offsets below");
     asm volatile(
         "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %17\n\t"
-        "ds_read_b64_tr_b16 %2, %16 offset:32\n\t"
-        "ds_read_b64_tr_b16 %3, %17 offset:32\n\t"
-        "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:64\n\t"
-        "ds_read_b64_tr_b16 %6, %16 offset:96\n\t"
-        "ds_read_b64_tr_b16 %7, %17 offset:96\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:4608\n\t"
         "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
-        "ds_read_b64_tr_b16 %9, %17 offset:128\n\t"
-        "ds_read_b64_tr_b16 %10, %16 offset:160\n\t"
-        "ds_read_b64_tr_b16 %11, %17 offset:160\n\t"
-        "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
-        "ds_read_b64_tr_b16 %13, %17 offset:192\n\t"
-        "ds_read_b64_tr_b16 %14, %16 offset:224\n\t"
-        "ds_read_b64_tr_b16 %15, %17 offset:224\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:4736\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:128\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:4736\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:128\n\t"
+        "ds_read_b64_tr_b16 %13, %18 offset:4736\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:128\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:4736\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
           "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
           "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
-        : "v"(a), "v"(b)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
   } else {
+    static_assert(VGeo<64>::TILE == 2560, "offsets below");
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:32\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:64\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
-        "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:2560\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
           "=&v"(lo[3]), "=&v"(hi[3])
-        : "v"(a), "v"(b)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
   }
 }
@@ -306,42 +336,108 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   };
   int vid = load_ids();
   const int ntiles = (p_end + kTP - 1) / kTP;
-  const int64_t blk_stride = (int64_t)hkv * BS * D;
   const uint16_t* kh_k = kc + (int64_t)kh * BS * D;
   const uint16_t* kh_v = vc + (int64_t)kh * BS * D;
 
-  // The workgroup's copies of tile j (positions clamped to p_end - 1) into
-  // stage sg, straight from HBM to LDS; wave w issues copies w, w + 4, ...
+  // The workgroup's copies of tile j into a stage, straight from HBM to LDS;
+  // wave w issues copies w, w + 4, ...  Copy k of this wave moves, for each
+  // lane, 16 bytes of tile row row0_of(k) + lane_row(k) at byte coff[k] of
+  // that row's (block, head) slice of the pool; tiles start at multiples of
+  // every block size, so the row's block is the tile's block row / BS.
+  constexpr int kCopies = SG::JOBS / kWaves;
+  // tile row of lane 0 of copy k (wave-uniform) and the lane's row above it
+  auto row0_of = [&](int k) -> int {
+    const int job = k * kWaves + w;
+    return job < SG::KJOBS ? kTile * (job / KC)
+                           : kTile * ((job - SG::KJOBS) / 4) + 4 * ((job - SG::KJOBS) % 4);
+  };
+  const int vrow = lane / VGeo<D>::CHUNKS;  // a V copy's row within its region
+  auto lane_row = [&](int k) -> int { return k * kWaves + w < SG::KJOBS ? col : vrow; };
+  uint32_t coff[kCopies];
+#pragma unroll
+  for (int k = 0; k < kCopies; ++k) {
+    const int job = k * kWaves + w;
+    const int row = row0_of(k) + lane_row(k);
+    if (job < SG::KJOBS) {
+      const int c = job % KC;
+      coff[k] = 2u * (uint32_t)((row % BS) * D + 32 * c + 8 * grp);
+    } else {
+      const int chunk = (lane % VGeo<D>::CHUNKS) ^ (2 * v_swizzle<D>(vrow));
+      coff[k] = 2u * (uint32_t)((row % BS) * D + chunk * 8);
+    }
+  }
+  const uint32_t blk_bytes = 2u * (uint32_t)hkv * BS * D;
+  const unsigned char* kh_kb = reinterpret_cast<const unsigned char*>(kh_k);
+  const unsigned char* kh_vb = reinterpret_cast<const unsigned char*>(kh_v);
+
   auto issue = [&](int j, unsigned char* stage) {
     const int t0 = j * kTP;
     if ((min(t0 + kTP, p_end) - 1) / BS - blk_base >= 64) {
       blk_base = t0 / BS;
       vid = load_ids();
     }
+    const int b0 = t0 / BS - blk_base;  // the tile's first block in vid
+    if (t0 + kTP <= p_end) {
+      // a whole tile: every row is in range, block ids are wave-uniform
+      // (one of two for the key copies at block size 8)
 #pragma unroll
-    for (int k = 0; k < SG::JOBS / kWaves; ++k) {
-      const int job = k * kWaves + w;
-      if (job < SG::KJOBS) {
-        const int sb = job / KC, c = job % KC;
-        const int t = min(t0 + kTile * sb + col, p_end - 1);
-        const int id = __shfl(vid, t / BS - blk_base);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(kh_k + id * blk_stride + (t % BS) * D + 32 * c + 8 * grp),
-            (void __attribute__((address_space(3)))*)(stage + job * SG::KBLK), 16, 0,
-            kCachePolicyStream);
-      } else {
-        const int vj = job - SG::KJOBS, sb = vj / 4, i = vj % 4;
-        const int t = min(t0 + kTile * sb + 4 * i + lane / (D / 8), p_end - 1);
-        const int id = __shfl(vid, t / BS - blk_base);
-        if (GE::LANES == 64 || lane < GE::LANES)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(kh_v + id * blk_stride + (t % BS) * D + (lane % (D / 8)) * 8),
-              (void __attribute__((address_space(3)))*)(stage + SG::KBYTES + sb * GE::TILE +
-                                                        i * GE::REGION),
-              16, 0, kCachePolicyStream);
+      for (int k = 0; k < kCopies; ++k) {
+        const int job = k * kWaves + w;
+        const bool is_k = job < SG::KJOBS;
+        const int bi = row0_of(k) / BS;  // lane 0's row is the lowest
+        const int id_lo = __builtin_amdgcn_readlane(vid, b0 + bi);
+        const unsigned char* pool = is_k ? kh_kb : kh_vb;
+        // the block's base in scalar registers, then the lane's offset (the
+        // empty asm keeps the compiler from hoisting a 64-bit pool + offset
+        // per copy into vector registers)
+        uint64_t base = (uint64_t)pool + (uint64_t)(uint32_t)id_lo * blk_bytes;
+        asm volatile("" : "+s"(base));
+        const unsigned char* src = (const unsigned char*)base + coff[k];
+        if constexpr (BS < kTile) {
+          if (is_k) {
+            const int id_hi = __builtin_amdgcn_readlane(vid, b0 + bi + 1);
+            uint64_t base_hi = (uint64_t)pool + (uint64_t)(uint32_t)id_hi * blk_bytes;
+            asm volatile("" : "+s"(base_hi));
+            if (col >= BS) src = (const unsigned char*)base_hi + coff[k];  // rows 16 sb + col
+          }
+        }
+        unsigned char* dst = is_k ? stage + job * SG::KBLK
+                                  : stage + SG::KBYTES + ((job - SG::KJOBS) / 4) * VGeo<D>::TILE +
+                                        ((job - SG::KJOBS) % 4) * VGeo<D>::REGION;
+        if (is_k || VGeo<D>::LANES == 64 || lane < VGeo<D>::LANES)
+          __builtin_amdgcn_global_load_lds((const void*)src,
+                                           (void __attribute__((address_space(3)))*)dst, 16, 0,
+                                           kCachePolicyStream);
       }
+      return;
+    }
+    // the unit's last tile: rows past p_end - 1 read row p_end - 1
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) {
+      const int job = k * kWaves + w;
+      const int row = row0_of(k) + lane_row(k);
+      const int t = min(t0 + row, p_end - 1);
+      const int id = __shfl(vid, t / BS - blk_base);
+      const unsigned char* pool = job < SG::KJOBS ? kh_kb : kh_vb;
+      const uint32_t off = coff[k] - 2u * (uint32_t)((row % BS) * D) + 2u * (uint32_t)((t % BS) * D);
+      const unsigned char* src = pool + (uint64_t)(uint32_t)id * blk_bytes + off;
+      unsigned char* dst = job < SG::KJOBS ? stage + job * SG::KBLK
+                                           : stage + SG::KBYTES + ((job - SG::KJOBS) / 4) * VGeo<D>::TILE +
+                                                 ((job - SG::KJOBS) % 4) * VGeo<D>::REGION;
+      if (job < SG::KJOBS || VGeo<D>::LANES == 64 || lane < VGeo<D>::LANES)
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (void __attribute__((address_space(3)))*)dst, 16, 0,
+                                         kCachePolicyStream);
     }
   };
+
+  // the lane's offsets, within a V sub-tile, of column blocks i ^ sw (i < 4)
+  // of rows 4 grp + (col >> 2): its transpose reads
+  uint32_t vlane[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    vlane[i] = (uint32_t)(grp * VGeo<D>::REGION + (col >> 2) * VGeo<D>::ROW + 8 * (col & 3) +
+                          32 * (i ^ v_swizzle<D>(col >> 2)));
 
   // The wave's row blocks over tile j, in slabs of 32 positions (two
   // sub-tiles): slabs past the wave's last position are skipped; each lane
@@ -409,10 +505,10 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
       }
       // V operand of column block m: rows 4 grp + r of the first sub-tile,
       // then of the second, column 16 m + col
-      const unsigned char* vb = stage + SG::KBYTES + 2 * sl * GE::TILE + grp * GE::REGION +
-                                (col >> 2) * GE::ROW + 8 * (col & 3);
+      const uint32_t vb = (uint32_t)(uintptr_t)(stage + SG::KBYTES + 2 * sl * VGeo<D>::TILE);
+      const uint32_t va[4] = {vb + vlane[0], vb + vlane[1], vb + vlane[2], vb + vlane[3]};
       uint2 vlo[NM], vhi[NM];
-      read_v_slab<NM>(vlo, vhi, vb, vb + GE::TILE);
+      read_v_slab<NM>(vlo, vhi, va);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint4 vop = make_uint4(vlo[m].x, vlo[m].y, vhi[m].x, vhi[m].y);
