@@ -33,7 +33,11 @@
 //
 // Placement: workgroup g runs on XCD g % 8; pair (s, kh) belongs to XCD
 // (s * hkv + kh) % 8, whose workgroups take its units consecutively (the
-// last, longest ones first), so the units of a pair share one L2.
+// last, longest ones first), so the units of a pair share one L2.  With at
+// most 64 pairs per XCD the pairs are taken in order of their sequence's
+// context before the chunk, longest first: a unit's time is mostly its
+// context, so the XCD's last units are its shortest (5% on the
+// chunked-prefill step, as a greedy-dispatch model of the units predicts).
 //
 // Copies: each lane's byte offset within a pool block is fixed per copy, so
 // a tile that lies wholly below the unit's last position costs a readlane of
@@ -49,7 +53,7 @@
 // tiles and the 16x16x32 P.V form 1.02 ms; the mask only on the diagonal,
 // the scale folded into one FMA per weight and the denominator on the
 // matrix cores 0.93 ms; scalar block addressing for whole tiles and the
-// swizzled V layout 0.86 ms.
+// swizzled V layout 0.85 ms; pairs ordered by context 0.80 ms.
 #include "pa_launch.h"
 #include "pa_mfma.h"
 
@@ -216,7 +220,34 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   const int un = blockIdx.x / 8;  // unit index within the XCD
   const int npairs = num_seqs * hkv;
   int s = -1, kh = 0, u_local = 0;
-  {
+  if (npairs <= 8 * 64) {
+    // at most 64 pairs on this XCD, one per lane: taken in order of their
+    // sequence's context before the chunk (L - n), longest first, ties by
+    // index, so the longest units start first and the XCD's last ones are
+    // short (a unit's time is mostly its context)
+    const int p = xcd + 8 * lane;
+    int cnt = 0, ctx = -1;
+    if (p < npairs) {
+      int qs_, n_;
+      chunk_of(p / hkv, qs_, n_);
+      cnt = (n_ + RW - 1) / RW;
+      if (cnt > 0) ctx = seq_lens[p / hkv] - n_;
+    }
+    int before = 0;  // units of the pairs taken before this lane's
+    for (int j = 0; j < 64; ++j) {
+      const int cj = __builtin_amdgcn_readlane(ctx, j);
+      const int nj = __builtin_amdgcn_readlane(cnt, j);
+      if (cj > ctx || (cj == ctx && j < lane)) before += nj;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(cnt > 0 && before <= un && un < before + cnt);
+    if (hit != 0) {
+      const int i = __builtin_ctzll(hit);
+      const int pp = xcd + 8 * i;
+      s = pp / hkv;
+      kh = pp % hkv;
+      u_local = un - __builtin_amdgcn_readlane(before, i);
+    }
+  } else {
     int run = 0;
     for (int j0 = 0; xcd + 8 * j0 < npairs; j0 += 64) {
       const int p = xcd + 8 * (j0 + lane);

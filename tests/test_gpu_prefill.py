@@ -8,7 +8,8 @@ mean-abs 1e-3: a chunk's first tokens see few positions, so their outputs
 can be as large as the values).
 
 Cases: whole prompts (chunk = sequence), chunks after a context, single-
-token chunks (decode), empty chunks, chunk lengths that are not multiples
+token chunks (decode), empty chunks, many sequences (more than 64
+(sequence, KV head) pairs per XCD, where units are not ordered by context), chunk lengths that are not multiples
 of the 16 / G tokens a unit holds, lengths around tile and block
 boundaries, every query group, head size, block size and output type; a
 chunk longer than its sequence and a block id outside the pool (NaN rows of
@@ -56,6 +57,10 @@ CASES = [
     ("g2_d64_bs16", [15, 16, 17, 0, 1], [1, 31, 33, 48, 2], 8, 4, 64, 16, "f16"),
     ("g8_d128_bs32", [0, 64, 1000, 7], [63, 0, 130, 1], 64, 8, 128, 32, "bf16"),
     ("decode_only", [50, 17, 16, 3, 1000], [1, 1, 1, 1, 1], 16, 4, 128, 16, "bf16"),
+    # more than 64 (sequence, KV head) pairs per XCD: units taken in pair order
+    # instead of by context length
+    ("many_pairs", [int(x) for x in np.random.default_rng(11).integers(0, 120, 70)],
+     [int(x) for x in np.random.default_rng(12).integers(0, 40, 70)], 16, 8, 64, 16, "bf16"),
 ]
 
 
