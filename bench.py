@@ -21,6 +21,13 @@ blocks, against the same loop holding 4096-token reservations; generated
 tokens per second of summed kernel time and of wall time, and the mean
 decode batch, for both.
 
+With --mode long the line is pa_decode over the long-context batch (32
+sequences of 8192..32768 tokens, 64 q / 8 KV heads) at block size 16; the
+default run adds every block size (8, 16, 32), balanced and with fixed
+512-position partitions, as the `long_context` object, and the shared-prefix
+step (copy-on-write + append + decode; cache-warm, logical and unique GB/s)
+as the `shared_prefix` object.
+
 With --kv fp8 the same step runs over 8-bit OCP E4M3 K/V pools (one scale
 per pool): pa_reshape_and_cache_fp8 + pa_decode_fp8, B_kv counted at one byte
 per element.  The default (16-bit) run also times that step and adds it as
@@ -138,11 +145,19 @@ def parse():
     ap.add_argument("--kv", choices=["16", "fp8"], default="16",
                     help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
                          "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
-    ap.add_argument("--mode", choices=["decode", "prefill", "serve"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "serve", "long"], default="decode",
                     help="decode: the mixed decode step (the headline); prefill: the chunked "
                          "prefill step (32 sequences x 512-token chunks, pa_prefill); serve: "
                          "iteration-level batching over the paged pool against 4096-token "
-                         "reservations on the same pool")
+                         "reservations on the same pool; long: decode over the long-context "
+                         "batch (32 sequences of 8192..32768 tokens, group 8) at block sizes "
+                         "8, 16 and 32")
+    ap.add_argument("--long-summary", choices=["on", "off"], default="on",
+                    help="with --mode decode: also time the long-context batch at block sizes "
+                         "8/16/32 and add a summary object")
+    ap.add_argument("--shared-summary", choices=["on", "off"], default="on",
+                    help="with --mode decode: also time the shared-prefix step (copy-on-write, "
+                         "append, decode) and add a summary object")
     ap.add_argument("--serve-iterations", type=int, default=300,
                     help="timed iterations per policy in --mode serve (after as many untimed)")
     ap.add_argument("--prefill-summary", choices=["on", "off"], default="on",
@@ -428,6 +443,137 @@ def prefill_line(args):
     return res
 
 
+def time_calls(fn, steps, warmup):
+    """Mean ms per call of fn over `steps` back-to-back calls after `warmup`
+    untimed ones: HIP events on the current stream around the whole run."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(steps):
+        fn()
+    c1.record()
+    torch.cuda.synchronize()
+    return c0.elapsed_time(c1) / steps
+
+
+LONG_WORKLOAD = ("long_context: 32 seqs, length uniform[8192,32768], 64 q / 8 kv heads "
+                 "(group 8), d 128, bf16 (f32 accumulate), block size 8, 16 and 32 with seeded "
+                 "random placement in a pool of blocks+10% (the same logical K/V for every "
+                 "block size), decode only")
+
+
+def long_context_summary(args, block_sizes=(8, 16, 32)):
+    """pa_decode over the long-context batch at each block size: the
+    balanced split (partition_size 0) and fixed 512-position partitions
+    merged by log-sum-exp, plus the gather-only ceiling of the balanced
+    split.  The batch's K/V (2.56 GB) is ten times the last-level cache, so
+    back-to-back calls read HBM."""
+    import torch
+    import paged_kv_cache_400_amd as pa
+    from paged_kv_cache_400_amd import workload as wl
+    res = {"workload": LONG_WORKLOAD + " (bench.py --mode long)"}
+    steps = max(1, min(args.steps, 50))
+    for bs in block_sizes:
+        b = wl.make_long_context(bs)
+        dev = wl.to_device(b, "cuda:0")
+        S, Hq, d = b.q.shape
+        kv = b.kv_bytes()
+        out = torch.empty_like(dev["q"])
+        row = {"kv_bytes": kv, "num_blocks": b.num_blocks,
+               "max_blocks_per_seq": b.max_blocks_per_seq}
+        for name, part in (("balanced", 0), ("partitions_512", 512)):
+            need = pa.decode_workspace_bytes(S, Hq, d, b.max_blocks_per_seq, bs, part)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
+            ms = time_calls(lambda: pa.decode(dev["q"], dev["k_cache"], dev["v_cache"],
+                                              dev["block_tables"], dev["seq_lens"],
+                                              scale=b.scale, partition_size=part, out=out,
+                                              workspace=ws), steps, args.warmup)
+            gbs = kv / (ms * 1e-3) / 1e9
+            row[name] = {"decode_ms": round(ms, 5), "gbs": round(gbs, 2),
+                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "decode_seqs_per_s": round(S / (ms * 1e-3), 1)}
+            del ws
+        if args.ceiling == "on":
+            sink = torch.zeros(2, dtype=torch.int16, device="cuda:0")
+            ms = time_calls(lambda: pa.probe_gather(dev["k_cache"], dev["v_cache"],
+                                                    dev["block_tables"], dev["seq_lens"], Hq,
+                                                    sink=sink), steps, args.warmup)
+            row["achievable_gbs"] = round(kv / (ms * 1e-3) / 1e9, 2)
+            row["balanced_frac_of_achievable"] = round(ms / row["balanced"]["decode_ms"], 4)
+        res[f"bs{bs}"] = row
+        del dev, out
+    return res
+
+
+SHARED_WORKLOAD = ("shared_prefix: 64 seqs sharing the physical blocks of a 2048-token prefix "
+                   "(odd-indexed seqs stop 1..15 tokens short of it and copy the partial block "
+                   "on write), private tails uniform[1,512], 32 q / 8 kv heads, d 128, fp16 "
+                   "(f32 accumulate), block 16")
+
+
+def unique_kv_bytes(b) -> int:
+    """K and V bytes of the distinct pool slots the batch's decode reads
+    (shared prefix slots counted once)."""
+    import numpy as np
+    bs = b.block_size
+    slots = []
+    for s, L in enumerate(b.seq_lens):
+        t = np.arange(int(L))
+        slots.append(b.block_tables[s, t // bs].astype(np.int64) * bs + t % bs)
+    n = len(np.unique(np.concatenate(slots))) if slots else 0
+    return int(n) * 2 * b.num_kv_heads * b.head_dim * b.elem_bytes
+
+
+def shared_prefix_summary(args):
+    """The shared-prefix step: copy-on-write of the 32 partial prefix blocks
+    (pa_copy_blocks), the tails' append (pa_reshape_and_cache) and pa_decode.
+    Repeating the step is idempotent (the copy restores what the append
+    overwrites).  Unique K/V (76 MB) stays in the last-level cache across
+    calls, so the figures are cache-warm: logical GB/s counts every
+    sequence's reads, unique GB/s each distinct slot once."""
+    import torch
+    import paged_kv_cache_400_amd as pa
+    from paged_kv_cache_400_amd import workload as wl
+    b = wl.make_shared_prefix()
+    dev = wl.to_device(b, "cuda:0")
+    S, Hq, d = b.q.shape
+    out = torch.empty_like(dev["q"])
+    need = pa.decode_workspace_bytes(S, Hq, d, b.max_blocks_per_seq, b.block_size, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
+
+    def copy_append():
+        pa.copy_blocks(dev["k_cache"], dev["v_cache"], dev["block_mapping"])
+        pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"],
+                             dev["v_cache"], dev["slot_mapping"])
+
+    def decode():
+        pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                  dev["seq_lens"], scale=b.scale, out=out, workspace=ws)
+
+    def step():
+        copy_append()
+        decode()
+
+    steps = max(1, min(args.steps, 50))
+    ms_step = time_calls(step, steps, args.warmup)
+    ms_copy_append = time_calls(copy_append, steps, args.warmup)
+    ms_decode = time_calls(decode, steps, args.warmup)
+    logical, unique = b.kv_bytes(), unique_kv_bytes(b)
+    return {
+        "workload": SHARED_WORKLOAD + " (cache-warm)",
+        "cow_pairs": int(len(b.block_mapping)), "appended_tokens": int(len(b.slot_mapping)),
+        "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+        "ms_per_step": round(ms_step, 5), "copy_append_ms": round(ms_copy_append, 5),
+        "decode_ms": round(ms_decode, 5),
+        "decode_logical_gbs": round(logical / (ms_decode * 1e-3) / 1e9, 2),
+        "decode_unique_gbs": round(unique / (ms_decode * 1e-3) / 1e9, 2),
+        "decode_seqs_per_s": round(S / (ms_decode * 1e-3), 1),
+    }
+
+
 SERVE_WORKLOAD = ("serve: a seeded stream of requests (prompts uniform[64,1024], generations "
                   "uniform[16,512], 8 arrivals per iteration), one attention layer of 32 q / 8 kv "
                   "heads, d 128, bf16, a pool of 4096 16-token blocks (65,536 tokens), at most "
@@ -474,6 +620,29 @@ def serve_line(args):
     }
 
 
+def long_line(args):
+    """The long-context batch as the line's workload: value = effective KV
+    GB/s of pa_decode (balanced split) at block size 16; every block size
+    and the fixed 512-position partitions in `long_context`."""
+    lc = long_context_summary(args)
+    row = lc["bs16"]["balanced"]
+    return {
+        "metric": METRIC, "value": row["gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": max(1, min(args.steps, 50)), "warmup": args.warmup,
+        "ms_per_step": row["decode_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": LONG_WORKLOAD, "block_size": 16,
+                   "kv_bytes": lc["bs16"]["kv_bytes"]},
+        "frac_of_hbm_peak": row["frac_of_hbm_peak"],
+        "decode_seqs_per_s": row["decode_seqs_per_s"],
+        "roofline": {"kernel": KERNEL_NAMES[("mfma", True)], "bound": "hbm",
+                     "achieved": row["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": row["frac_of_hbm_peak"], "traffic": None,
+                     "traffic_source": "not profiled"},
+        "long_context": lc,
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -491,6 +660,9 @@ def main():
         return
     if args.mode == "serve":
         print(json.dumps(serve_line(args)), flush=True)
+        return
+    if args.mode == "long":
+        print(json.dumps(long_line(args)), flush=True)
         return
 
     b = wl.make_mixed_step(kv=args.kv)
@@ -599,6 +771,10 @@ def main():
             "tokens_per_s": round(int(pf.query_start[-1]) / (sp * 1e-3), 1),
         }
         del devp
+    if args.long_summary == "on" and profiled and args.kv == "16":
+        res["long_context"] = long_context_summary(args)
+    if args.shared_summary == "on" and profiled and args.kv == "16":
+        res["shared_prefix"] = shared_prefix_summary(args)
     if args.block_manager == "on":
         res["host_block_manager"] = host_block_manager(b)
         res["host_block_manager"]["frac_of_step"] = round(
