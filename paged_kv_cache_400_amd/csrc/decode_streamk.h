@@ -11,8 +11,8 @@
 //
 // Tile order: for each KV head, the sequences' tiles back to back, sequence
 // s holding ceil(L_s / n) tiles of n positions (n = 16 for 16-bit pools, 32
-// for 8-bit ones).  The launch has as many waves as the GPU keeps resident
-// (a whole number per KV head); wave w works on head w % hkv and takes the
+// for 8-bit ones).  The launch has two workgroups (8 waves) per CU, all
+// resident at once (a whole number of waves per KV head); wave w works on head w % hkv and takes the
 // (w / hkv)-th of that head's equal runs of C = ceil(tiles per head / waves
 // per head) tiles (at least kMinChunk).  Adjacent waves therefore read the
 // same positions of adjacent heads, neighbouring pieces of the same pool
@@ -98,9 +98,12 @@ struct TileWaveOf<T, FP8, D, BS, G> {
 // results (a word is written to `out` only if the XOR of the loaded data hits
 // a value it cannot be expected to hit).  KV is the pool element type (T, or
 // FP8 with out_scale = v_scale applied to every result; for 16-bit pools
-// out_scale is not used).
+// out_scale is not used).  Two waves per SIMD are all the launch uses
+// (kWorkgroupsPerCu), so the compiler may take up to 256 registers; the
+// 8-bit tile wave uses 190 of them (with the 168 that three waves allow it
+// spent 8% more time on the mixed step), the 16-bit one about 150.
 template <typename T, int D, int BS, int G, bool kGather, typename KV>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   float2* __restrict__ ws_ml, int4* __restrict__ ws_meta,
                   const uint16_t* __restrict__ q,
@@ -379,11 +382,22 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
 }
 
 // ---------------------------------------------------------------------------
-// Resident waves of one decode instantiation on the current device (cached
-// per instantiation and device; recomputing it gives the same value, so
-// concurrent first calls are harmless).
+// Workgroups per CU the launch uses: two (8 waves), not the three that fit.
+// The K/V gather saturates with as few as 4 waves per CU (the gather-only
+// probe takes the same time with 4 to 20), so the third workgroup adds no
+// loads in flight that the memory system can use; it only makes the runs a
+// third shorter (more pairs cut, more partials, more wave starts) and puts
+// a third more waves on each SIMD.  Measured with two instead of three:
+// mixed decode step 358 -> 346 us, the same over 8-bit pools 222 -> 204 us,
+// long context at block 16 416 -> 394 us.
+constexpr int kWorkgroupsPerCu = 2;
+
+// Waves of one decode launch on the current device: kWorkgroupsPerCu
+// workgroups per CU, or fewer if fewer fit (cached per instantiation and
+// device; recomputing it gives the same value, so concurrent first calls are
+// harmless).
 template <typename T, typename KV, int D, int BS, int G>
-static int resident_waves() {
+static int launch_waves() {
   constexpr int kMaxDevices = 64;
   static int cache[kMaxDevices];
   int dev = 0;
@@ -396,7 +410,7 @@ static int resident_waves() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, pa_decode_streamk<T, D, BS, G, false, KV>, kThreads, 0) != hipSuccess)
     return 0;
-  const int waves = cus * max(per_cu, 1) * kWaves;
+  const int waves = cus * max(min(per_cu, kWorkgroupsPerCu), 1) * kWaves;
   __atomic_store_n(&cache[dev], waves, __ATOMIC_RELAXED);
   return waves;
 }
@@ -404,7 +418,7 @@ static int resident_waves() {
 template <typename T, typename KV, int D, int BS, int G>
 static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
-  int waves = resident_waves<T, KV, D, BS, G>();
+  int waves = launch_waves<T, KV, D, BS, G>();
   if (waves <= 0) return hipErrorInvalidDevice;
   if (a.num_kv_heads > kStreamKMaxWaves) return hipErrorInvalidValue;
   // a whole number of waves per KV head, at least one
