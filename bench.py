@@ -84,7 +84,8 @@ KERNEL_SOURCES = {
 KERNEL_NAMES = {
     ("fp8", True): "pa_decode_fp8 (pa_decode_streamk over E4M3 pools + pa_streamk_reduce)",
     ("mfma", True): "pa_decode (pa_decode_streamk + pa_streamk_reduce)",
-    ("mfma", False): "pa_decode, explicit partitions (pa_decode_mfma + pa_splitk_reduce)",
+    ("mfma", False): ("pa_decode, explicit partitions (pa_decode_streamk with runs cut at "
+                      "partition boundaries + pa_streamk_reduce)"),
     ("valu", True): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
     ("valu", False): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
 }

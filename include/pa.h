@@ -95,14 +95,17 @@ typedef enum pa_dtype {
  * Supported: dtype F16/BF16 (q, pools and out share it); head_dim 64 or
  * 128; block_size 8, 16 or 32; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  *
- * Work split.  partition_size = 0 (automatic) selects the balanced split:
- * the (sequence, KV head) pairs are laid end to end as tiles of 16
- * positions and every resident wave of the GPU takes an equal run of them;
- * a pair cut between runs leaves partial softmax states that a second kernel
- * merges by log-sum-exp.  partition_size > 0 (a multiple of 16 and of
- * block_size, at most 512 blocks) selects fixed partitions of that many
- * positions per (sequence, KV head), merged the same way.  Both give the
- * same result up to float32 summation order.  The workspace needs
+ * Work split: the balanced split.  For each KV head the sequences are laid
+ * end to end as tiles of 16 positions, and each of the launch's waves (eight
+ * per CU) takes an equal run of them.  A (sequence, KV head) pair cut
+ * between runs leaves partial softmax states that a second kernel merges by
+ * log-sum-exp.  partition_size = 0 (automatic) lets runs start and end at
+ * any tile.  partition_size > 0 (a multiple of 16 and of block_size, at
+ * most 512 blocks) makes each sequence a series of partitions of that many
+ * positions ([k*P, (k+1)*P)), and runs start and end only at partition
+ * boundaries: every partial state covers whole partitions, and the
+ * partitions one wave walks in a sequence are merged in its registers.
+ * Both give the same result up to float32 summation order.  The workspace needs
  * pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents on
  * entry do not matter and on return are unspecified.
  *
@@ -134,14 +137,14 @@ pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const vo
 
 /*
  * Workspace bytes pa_decode (and pa_decode_valu) need for these sizes; no
- * device memory is read.  partition_size > 0: (m, l, acc) per (sequence,
- * query head, partition), an upper bound from max_blocks_per_seq *
- * block_size, 0 when no sequence can need more than one partition.
- * partition_size = 0: the balanced split's partial states (two per wave, at
- * most 8192 waves, min(num_q_heads, 8) heads each) and one 16-byte record
- * per (sequence, query head), or the 512-position partitions
- * pa_decode_valu uses in that mode, whichever is larger.  0 when an argument
- * is invalid (pa_decode then reports the error).
+ * device memory is read.  The larger of: the balanced split's partial
+ * states (two per wave, at most 8192 waves, min(num_q_heads, 8) heads each)
+ * and one 16-byte record per (sequence, query head), which pa_decode uses;
+ * and the (m, l, acc) per (sequence, query head, partition) of
+ * pa_decode_valu's fixed partitions (of partition_size positions, 512 when
+ * it is 0), an upper bound from max_blocks_per_seq * block_size that is 0
+ * when no sequence can need more than one partition.  0 when an argument is
+ * invalid (pa_decode then reports the error).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_blocks_per_seq, int32_t block_size,

@@ -1,9 +1,10 @@
 // decode_streamk.h -- paged decode attention, the balanced (stream-K)
-// decomposition used by pa_decode when partition_size is 0 (and by
-// pa_decode_fp8), as templates: decode_streamk.hip instantiates them for
-// 16-bit pools, decode_fp8.hip for 8-bit E4M3 pools.
+// decomposition used by pa_decode (runs cut at partition boundaries when
+// partition_size is given) and by pa_decode_fp8, as templates:
+// decode_streamk.hip instantiates them for 16-bit pools, decode_fp8.hip for
+// 8-bit E4M3 pools.
 //
-// What is computed is the same as the partitioned kernels: for every
+// What is computed is the same as the vector kernel's: for every
 // sequence s and query head h, softmax attention of q[s][h] over positions
 // 0..L_s-1 read through the sequence's block table ("What problem does
 // PagedAttention solve ...", section "How PagedAttention works").  What
@@ -111,7 +112,8 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   const typename TileWaveOf<T, KV, D, BS, G>::type::Elem* __restrict__ vc,
                   const int32_t* __restrict__ block_tables,
                   const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t hkv,
-                  int32_t mb, int32_t nb, int32_t nwaves, float qk_scale, float out_scale) {
+                  int32_t mb, int32_t nb, int32_t nwaves, int32_t part_tiles, float qk_scale,
+                  float out_scale) {
   using TW = typename TileWaveOf<T, KV, D, BS, G>::type;
   constexpr int KL = TW::KL, NM = TW::NM, kT = TW::kTileLen, kIds = TW::kIds;
   constexpr bool kScaled = !std::is_same<KV, T>::value;
@@ -127,47 +129,70 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   };
 
   // ---- this wave's run: wave w works on KV head w % hkv, and the waves of
-  // one head split that head's tile order (the sequences' tiles back to
-  // back) into equal runs.  Adjacent waves take adjacent heads of the same
-  // positions, so they read neighbouring pieces of the same pool blocks at
-  // about the same time.
+  // one head split that head's order of units (the sequences' units back to
+  // back) into equal runs.  A unit is one tile, or with part_tiles > 0 a
+  // partition of part_tiles tiles (the last of a sequence may be shorter):
+  // runs then start and end only at partition boundaries, and the
+  // partitions a wave walks in one sequence are merged in its registers.
+  // Adjacent waves take adjacent heads of the same positions, so they read
+  // neighbouring pieces of the same pool blocks at about the same time.
+  const int pt = part_tiles > 0 ? part_tiles : 1;  // tiles per unit
+  auto units_of = [&](int L) -> int { return (tiles_of(L) + pt - 1) / pt; };
   const int nwh = nwaves / hkv;  // waves per head (the launch has nwaves >= hkv)
   const int kh0 = wave % hkv, jw = wave / hkv;
   if (jw >= nwh) return;
-  int64_t per_head = 0;  // sum over sequences of their tile counts
+  int64_t per_head = 0, per_head_tiles = 0;  // units and tiles of all sequences
   for (int b = 0; b < num_seqs; b += 64) {
-    const int n = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) : 0;
-    per_head += wave_sum(n);
+    const int L = (b + lane < num_seqs) ? seq_lens[b + lane] : 0;
+    per_head += wave_sum(units_of(L));
+    per_head_tiles += wave_sum(tiles_of(L));
   }
-  const int64_t chunk = max((int64_t)kMinChunk, (per_head + nwh - 1) / nwh);
-  const int64_t g0 = (int64_t)jw * chunk;
-  if (g0 >= per_head) return;
-  const int64_t g1 = min(per_head, g0 + chunk);
+  const int64_t chunk =
+      max((int64_t)(pt == 1 ? kMinChunk : 1), (per_head + nwh - 1) / nwh);  // units per run
+  const int64_t u0 = (int64_t)jw * chunk;
+  if (u0 >= per_head) return;
+  const int64_t u1 = min(per_head, u0 + chunk);
 
-  // first sequence whose tiles reach past g0, and where its tiles start
-  int s = -1;
-  int64_t seq_start = 0;  // index of the sequence's first tile in the head's order
-  {
-    int64_t run = 0;
+  // The sequence holding unit u, where its units start, and where its tiles
+  // start (index of its first unit / tile in the head's order).
+  struct Where { int s; int64_t ustart, tstart; };
+  auto locate = [&](int64_t u) -> Where {
+    int64_t urun = 0, trun = 0;
     for (int b = 0; b < num_seqs; b += 64) {
-      const int span = (b + lane < num_seqs) ? tiles_of(seq_lens[b + lane]) : 0;
-      const int incl = wave_inclusive_scan(span, lane);
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(run + incl > g0);
+      const int L = (b + lane < num_seqs) ? seq_lens[b + lane] : 0;
+      const int un = units_of(L), tn = tiles_of(L);
+      const int uincl = wave_inclusive_scan(un, lane);
+      const int tincl = wave_inclusive_scan(tn, lane);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(urun + uincl > u);
       if (hit != 0) {
         const int i = __builtin_ctzll(hit);
-        s = b + i;
-        seq_start = run + lane_value(incl, i) - lane_value(span, i);
-        break;
+        return {b + i, urun + lane_value(uincl, i) - lane_value(un, i),
+                trun + lane_value(tincl, i) - lane_value(tn, i)};
       }
-      run += lane_value(incl, 63);
+      urun += lane_value(uincl, 63);
+      trun += lane_value(tincl, 63);
+    }
+    return {-1, urun, trun};
+  };
+  const Where w0 = locate(u0);
+  int s = w0.s;
+  if (s < 0) return;  // unreachable: u0 < per_head
+  int64_t seq_ustart = w0.ustart;  // the current sequence's first unit
+  const int64_t g0 = w0.tstart + (u0 - w0.ustart) * pt;  // the run's first tile
+  int64_t g1 = per_head_tiles;                          // one past its last tile
+  if (u1 < per_head) {
+    if (pt == 1) {
+      g1 = u1;
+    } else {
+      const Where w1 = locate(u1);
+      g1 = w1.tstart + (u1 - w1.ustart) * pt;
     }
   }
-  if (s < 0) return;  // unreachable: g0 < per_head
   int L = seq_lens[s];
   int ns = tiles_of(L);
-  if (ns == 0) return;  // unreachable: the first hit has tiles
+  if (ns == 0) return;  // unreachable: the first hit has units
   const int kh = kh0;
-  int t_lo = (int)(g0 - seq_start);
+  int t_lo = (int)(g0 - w0.tstart);
 
   // The segment's result: final rows for a pair wholly inside the run, else
   // a partial in slot 0 (the run's first pair) or 1 (its last); the wave
@@ -177,7 +202,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   // consumed) and stored 16 bytes per lane: whole, contiguous cache lines.
   // (Stores of 32 or 64 bytes per instruction cost the mixed decode step 2%.)
   auto write_result = [&](const TW& t, bool bad, int64_t row0, int t_lo,
-                          int t_hi, int ns, bool first, int64_t pair_start) {
+                          int t_hi, int ns, bool first, int64_t pair_ustart) {
     const int col = lane & 15, grp = lane >> 4;
     const bool whole = t_lo == 0 && t_hi == ns;
     float* st = reinterpret_cast<float*>(t.vtile);  // [G][D]
@@ -212,9 +237,9 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
         ws_ml[slot * G + lane] = make_float2(t.m_run, bad ? __builtin_nanf("") : t.l_run);
     }
     if (t_hi == ns && lane == 0) {
-      const int c_first = (int)(pair_start / chunk);
-      const int c_last = (int)((pair_start + ns - 1) / chunk);
-      ws_meta[row0 / G] = make_int4(c_first, c_last, pair_start % chunk != 0, 0);
+      const int c_first = (int)(pair_ustart / chunk);
+      const int c_last = (int)((pair_ustart + (ns + pt - 1) / pt - 1) / chunk);
+      ws_meta[row0 / G] = make_int4(c_first, c_last, pair_ustart % chunk != 0, 0);
     }
   };
   static_assert(sizeof(float) * G * D <= 2 * TW::kTileBytes, "the result fits the wave's V tiles");
@@ -225,7 +250,6 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   int64_t g = g0;
   while (true) {
     // ---- one segment: pair (s, kh), tiles [t_lo, t_hi)
-    const int64_t pair_start = g - t_lo;  // global index of the pair's tile 0
     const int t_hi = (int)min((int64_t)ns, (int64_t)t_lo + (g1 - g));
     const int p_lo = t_lo * kT;
     const int p_end = min(L, t_hi * kT);  // positions [p_lo, p_end)
@@ -299,13 +323,14 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       if (gathered == 0x9e3779b9u && lane == 0) out[0] = (uint16_t)gathered;
     } else {
       tw.finish();
-      write_result(tw, bad, row0, t_lo, t_hi, ns, g == g0, pair_start);
+      write_result(tw, bad, row0, t_lo, t_hi, ns, g == g0, seq_ustart);
     }
 
     g += ntiles;
     if (g >= g1) break;
     // the run goes on, so this sequence ended here: the next one, same head
     t_lo = 0;
+    seq_ustart += (ns + pt - 1) / pt;
     do {
       if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
       L = seq_lens[s];
@@ -429,7 +454,7 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                        dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
                        nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                        a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
-                       a.max_blocks_per_seq, a.num_blocks, waves, 0.0f, 0.0f);
+                       a.max_blocks_per_seq, a.num_blocks, waves, 0, 0.0f, 0.0f);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>),
@@ -437,7 +462,8 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                      dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
                      (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                      a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
-                     a.max_blocks_per_seq, a.num_blocks, waves, a.qk_scale, a.out_scale);
+                     a.max_blocks_per_seq, a.num_blocks, waves, a.part_tiles, a.qk_scale,
+                     a.out_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pa_streamk_reduce<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),

@@ -40,8 +40,8 @@ int64_t partitions_needed(int32_t max_blocks_per_seq, int32_t block_size, int32_
   return (max_len + part - 1) / part;
 }
 
-// Workspace of the partitioned kernels: (m, l, acc) per (sequence, query
-// head, partition); 0 when no sequence can need more than one partition or
+// Workspace of the fixed partitions of pa_decode_valu: (m, l, acc) per
+// (sequence, query head, partition); 0 when no sequence can need more than one partition or
 // the partition size is invalid.
 size_t partitioned_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                    int32_t max_blocks_per_seq, int32_t block_size,
@@ -83,14 +83,15 @@ int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_blocks_per_seq, int32_t block_size,
                                  int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0)
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      resolve_partition(partition_size, block_size) == 0)
     return 0;
   const size_t part_bytes = partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim,
                                                         max_blocks_per_seq, block_size,
                                                         partition_size);
-  if (partition_size != 0) return part_bytes;
-  // automatic: pa_decode runs the balanced kernel, pa_decode_valu 512-position
-  // partitions; the workspace serves either
+  // pa_decode runs the balanced kernel (partition-aligned runs when
+  // partition_size > 0), pa_decode_valu fixed partitions (512 positions when
+  // partition_size is 0); the workspace serves either
   const size_t sk = (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim);
   return sk > part_bytes ? sk : part_bytes;
 }
@@ -151,7 +152,7 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
   if (units * 256 >= kMaxThreadsPerLaunch || pmax > INT32_MAX)
     return fail(PA_ERR_SHAPE, "pa_decode: %lld work units exceed one launch",
                 (long long)units);
-  const bool balanced = impl == Impl::kMfma && partition_size == 0;
+  const bool balanced = impl == Impl::kMfma;
   const size_t need =
       balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim)
                : partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
@@ -182,6 +183,7 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
+    a.part_tiles = partition_size / 16;  // 16-position tiles (the 16-bit decode's)
     a.qk_scale = scale * 1.4426950408889634f * (kv_fp8 ? k_scale : 1.0f);
     a.out_scale = v_scale;
     a.bf16 = dtype == PA_BF16;
@@ -214,7 +216,7 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
   a.qk_scale = scale * 1.4426950408889634f;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = impl == Impl::kMfma ? pa::launch_decode_mfma(a) : pa::launch_decode(a);
+  const hipError_t e = pa::launch_decode(a);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -41,6 +41,7 @@ struct StreamKArgs {
   int4* ws_meta;
   int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
   int32_t max_blocks_per_seq, num_blocks;
+  int32_t part_tiles; // 0: runs cut at any tile; else only at multiples of this many tiles
   float qk_scale;     // scale * log2(e) (* k_scale for 8-bit pools)
   float out_scale;    // v_scale for 8-bit pools (unused for 16-bit pools)
   bool bf16;          // q and out bf16 (else fp16)
@@ -88,10 +89,9 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // Waves the prefill launch has (an upper bound on its units).
 int64_t prefill_units(int32_t total_q, int32_t num_seqs, int32_t num_kv_heads, int32_t group);
 
-// pa_decode_valu kernel (decode.hip) and pa_decode_mfma kernel
-// (decode_mfma.hip); each launches the split-K merge itself when pmax > 1.
+// pa_decode_valu kernel (decode.hip); it launches the split-K merge itself
+// when pmax > 1.
 hipError_t launch_decode(const DecodeArgs& a);
-hipError_t launch_decode_mfma(const DecodeArgs& a);
 hipError_t launch_splitk_reduce(const DecodeArgs& a);
 int decode_max_partition_blocks();
 

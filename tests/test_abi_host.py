@@ -69,22 +69,24 @@ def test_one_hip_runtime_is_mapped(lib):
 
 def test_workspace_bytes(lib):
     f = lib.pa_decode_workspace_bytes
-    # explicit partitions: (m, l, acc) per (sequence, query head, partition)
-    # 257 blocks of 16 = 4112 tokens -> 9 partitions of 512
-    assert f(256, 32, 128, 257, 16, 512) == 256 * 32 * 9 * (128 + 2) * 4
-    assert f(32, 64, 128, 2048, 16, 512) == 32 * 64 * 64 * 130 * 4
-    assert f(2, 4, 64, 10, 8, 16) == 2 * 4 * 5 * 66 * 4
-    assert f(4, 8, 64, 4, 16, 512) == 0         # one partition: no workspace
-    assert f(2, 4, 64, 10, 8, 12) == 0          # not a multiple of the block size
-    assert f(2, 4, 64, 10, 8, 8 * 513) == 0     # more blocks than a partition holds
 
-    # automatic: the balanced kernel's two partial slots per wave (at most
-    # 8192 waves, min(Hq, 8) heads of d floats + (m, l) each) and one 16-byte
-    # record per (sequence, query head); or the 512-position partitions of
-    # pa_decode_valu, whichever is larger
+    # pa_decode's balanced split: two partial slots per wave (at most 8192
+    # waves, min(Hq, 8) heads of d floats + (m, l) each) and one 16-byte
+    # record per (sequence, query head), with or without partition_size
     def balanced(S, Hq, d):
         return 2 * 8192 * min(Hq, 8) * (d * 4 + 8) + S * Hq * 16
 
+    # pa_decode_valu's fixed partitions: (m, l, acc) per (sequence, query head,
+    # partition); the larger of the two is returned
+    # 257 blocks of 16 = 4112 tokens -> 9 partitions of 512
+    assert f(256, 32, 128, 257, 16, 512) == max(balanced(256, 32, 128), 256 * 32 * 9 * 130 * 4)
+    assert f(32, 64, 128, 2048, 16, 512) == max(balanced(32, 64, 128), 32 * 64 * 64 * 130 * 4)
+    assert f(2, 4, 64, 10, 8, 16) == max(balanced(2, 4, 64), 2 * 4 * 5 * 66 * 4)
+    assert f(4, 8, 64, 4, 16, 512) == balanced(4, 8, 64)   # one partition: balanced only
+    assert f(2, 4, 64, 10, 8, 12) == 0          # not a multiple of the block size
+    assert f(2, 4, 64, 10, 8, 8 * 513) == 0     # more blocks than a partition holds
+
+    # automatic: pa_decode_valu uses 512-position partitions
     assert f(4, 8, 64, 4, 16, 0) == balanced(4, 8, 64)
     assert f(256, 32, 128, 257, 16, 0) == max(balanced(256, 32, 128), 256 * 32 * 9 * 130 * 4)
     assert f(8, 2, 128, 4096, 8, 0) == max(balanced(8, 2, 128), 8 * 2 * 64 * 130 * 4)

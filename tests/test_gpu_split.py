@@ -7,7 +7,9 @@ stress them, against the float64 CPU oracle (max-abs <= 1e-2, mean-abs <=
     sequences crosses several 64-sequence chunks; one long sequence on one KV
     head, cut across hundreds of waves, so the merge combines hundreds of
     partials; empty sequences between non-empty ones;
-  * fixed partitions (partition_size > 0) on the same inputs;
+  * explicit partitions (partition_size 64 and 512) on the same inputs: the
+    runs then start and end only at partition boundaries, so one long
+    sequence is merged from one partial per run of whole partitions;
   * contract violations the kernels guard against (a length past the block
     table, a block id outside the pool): that sequence's rows are NaN, no
     other row changes.
