@@ -13,26 +13,28 @@
 // Tile order: for each KV head, the sequences' tiles back to back, sequence
 // s holding ceil(L_s / n) tiles of n positions (n = 16 for 16-bit pools, 32
 // for 8-bit ones).  The launch has two workgroups (8 waves) per CU, all
-// resident at once (a whole number of waves per KV head); wave w works on head w % hkv and takes the
-// (w / hkv)-th of that head's equal runs of C = ceil(tiles per head / waves
-// per head) tiles (at least kMinChunk).  Adjacent waves therefore read the
-// same positions of adjacent heads, neighbouring pieces of the same pool
-// blocks, at about the same time: 2% faster on the mixed decode step than
-// the pairs in (sequence, head) order, 4% with 8-bit pools.  Every wave
-// streams the same number of tiles (to one tile), never waits for another
-// wave, and never sits idle at the end of a work unit: the partitioned
-// kernels spend a merge through LDS and a barrier on every (sequence, head,
-// 512-position) unit, and their units differ in size.  Each wave finds its
-// first sequence from a prefix sum of the tile counts (recomputed by every
-// wave from seq_lens; a few hundred integers from L2), then walks its run
-// sequence by sequence:
+// resident at once (a whole number of waves per KV head); wave w works on
+// head w % hkv and takes the (w / hkv)-th of that head's equal runs of
+// units.  A unit is a tile, or with an explicit partition_size a partition
+// of that many positions (runs then start and end only at partition
+// boundaries).  Adjacent waves therefore read the same positions of
+// adjacent heads, neighbouring pieces of the same pool blocks, at about the
+// same time: 2% faster on the mixed decode step than the pairs in
+// (sequence, head) order, 4% with 8-bit pools.  Every wave streams the same
+// number of units, never waits for another wave, and never sits idle at the
+// end of a work unit: a kernel with one workgroup per (sequence, head,
+// 512-position) unit spent a merge through LDS and a barrier on every unit,
+// and its units differed in size.  Each wave finds its first sequence from
+// a prefix sum of the unit counts (recomputed by every wave from seq_lens; a
+// few hundred integers from L2), then walks its run sequence by sequence:
 //   - a pair that lies wholly inside the run is finished in place: out =
 //     acc / l, rounded to the output type;
 //   - a pair cut by the run's start or end leaves a partial (m, l, acc) in
 //     the wave's slot 0 (the pair it starts in) or slot 1 (the pair it ends
 //     in) of the workspace;
 //   - the wave that processes a pair's last tile records which runs of the
-//     head hold its partials (meta; run c of head kh is wave c * hkv + kh),
+//     head hold its partials (meta; run c of head kh is wave c * hkv + kh,
+//     and unit u of the head's order lies in run u / C, C units per run),
 //     and pa_streamk_reduce merges them by log-sum-exp
 //     ("Continuous Batching & Paged Attention", section "Attention needs
 //     memory that grows with the conversation": plain softmax attention; the
