@@ -95,18 +95,6 @@ def compare(out_gpu, ref, pairs=None, label="", round_slack=False, value_scale=1
     return mx, mean
 
 
-def sample_pairs(b, n_seqs, seed=0):
-    """All query heads of n_seqs sequences: the shortest, the longest, and a
-    seeded random choice of the rest."""
-    rng = np.random.default_rng(seed)
-    order = np.argsort(b.seq_lens, kind="stable")
-    pick = {int(order[0]), int(order[-1])}
-    rest = [s for s in range(b.num_seqs) if s not in pick]
-    pick |= set(int(x) for x in rng.choice(rest, size=min(len(rest), n_seqs - len(pick)),
-                                           replace=False))
-    return np.array([(s, h) for s in sorted(pick) for h in range(b.num_q_heads)], np.int32)
-
-
 # ---- 8-bit (E4M3) pools
 
 def gpu_step_fp8(b, device="cuda:0", dev=None):
