@@ -135,7 +135,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default 10; 50 with --mode prefill, whose "
-                         "matrix-core kernel runs below full clock for its first ~20 ms)")
+                         "matrix-core kernel runs below full clock for its first ~20 ms, "
+                         "and with --kv fp8, whose first ~10 ms run below full clock too)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--ceiling", choices=["on", "off"], default="on",
                     help="also time pa_probe_gather (the same loads, no arithmetic)")
@@ -175,7 +176,8 @@ def parse():
                          "known size to scale HBM byte counters by)")
     args = ap.parse_args()
     if args.warmup is None:
-        args.warmup = PREFILL_WARMUP if args.mode == "prefill" else 10
+        args.warmup = (PREFILL_WARMUP if args.mode == "prefill" else
+                       FP8_WARMUP if args.kv == "fp8" else 10)
     return args
 
 
@@ -245,7 +247,7 @@ def host_block_manager(b, steps=200):
             "ops": "append_batch (one token per sequence) + tables, through the Python binding"}
 
 
-def measure(b, dev, args, kv, partition_size, with_ceiling):
+def measure(b, dev, args, kv, partition_size, with_ceiling, warmup=None):
     """Time K steps (append + decode) of batch b after W warmup steps, HIP
     events on the current stream around the whole run and around each decode
     call; then, optionally, K gather-only runs.  Returns (ms per step, ms per
@@ -277,7 +279,8 @@ def measure(b, dev, args, kv, partition_size, with_ceiling):
                       dev["seq_lens"], scale=b.scale, partition_size=partition_size, out=out,
                       workspace=ws, impl=args.impl)
 
-    for _ in range(args.warmup):
+    W = args.warmup if warmup is None else warmup
+    for _ in range(W):
         append()
         decode()
     torch.cuda.synchronize()
@@ -302,7 +305,7 @@ def measure(b, dev, args, kv, partition_size, with_ceiling):
     ceiling = None
     if with_ceiling:
         sink = torch.zeros(2, dtype=torch.int16, device="cuda:0")
-        for _ in range(args.warmup):
+        for _ in range(W):
             pa.probe_gather(dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
                             Hq, sink=sink)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -339,6 +342,11 @@ def calibration_copy(mib):
 # 20 ms of matrix-core work to settle (per-dispatch durations fall by a
 # quarter over the first 20 steps, then stay flat).
 PREFILL_WARMUP = 50
+
+# Warmup steps of an 8-bit decode measurement: the first ~10 ms after the
+# host has prepared the batch run below full clock (the first repetition of
+# 100 calls averages 198 us, the next ones 190 us); 50 steps are ~10 ms.
+FP8_WARMUP = 50
 
 
 def measure_prefill(b, dev, args, warmup=None):
@@ -742,11 +750,13 @@ def main():
         del dev
         b8 = wl.make_mixed_step(kv="fp8")
         dev8 = wl.to_device(b8, "cuda:0")
-        s8, d8, c8 = measure(b8, dev8, args, "fp8", 0, args.ceiling == "on")
+        s8, d8, c8 = measure(b8, dev8, args, "fp8", 0, args.ceiling == "on",
+                             warmup=max(args.warmup, FP8_WARMUP))
         kv8 = b8.kv_bytes()
         res["fp8_kv"] = {
             "workload": "the same step over 8-bit E4M3 K/V pools (bench.py --kv fp8)",
             "kv_bytes": kv8,
+            "warmup": max(args.warmup, FP8_WARMUP),
             "ms_per_step": round(s8, 5),
             "value_gbs": round(kv8 / (s8 * 1e-3) / 1e9, 2),
             "decode_ms": round(d8, 5),
