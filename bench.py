@@ -41,7 +41,9 @@ Prints one JSON line:
               HIP events on its stream over the timed steps) against the
               8 TB/s HBM peak; `achievable` is the same figure for
               pa_probe_gather, which issues exactly pa_decode's K/V loads and
-              computes nothing (the gather pattern's own ceiling)
+              computes nothing (the gather pattern's own ceiling);
+              `streaming_read` the same for pa_probe_stream, a plain
+              streaming read of as many bytes (the device's read peak)
   cpu_baseline  the float64 CPU oracle on the same step, host cores
   host_block_manager  the host bookkeeping of the same step through the
               block manager (include/pa_block_manager.h): one appended
@@ -318,6 +320,18 @@ def measure(b, dev, args, kv, partition_size, with_ceiling, warmup=None):
         torch.cuda.synchronize()
         ceiling = c0.elapsed_time(c1) / K
     return ms_step, ms_decode, ceiling
+
+
+def streaming_read(nbytes, steps, warmup):
+    """Mean us per pa_probe_stream call over a device buffer of nbytes bytes
+    (HIP events around `steps` back-to-back calls after `warmup`)."""
+    import torch
+    import paged_kv_cache_400_amd as pa
+    buf = torch.empty(nbytes // 16 * 16, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(2, dtype=torch.int16, device="cuda:0")
+    ms = time_calls(lambda: pa.probe_stream(buf, sink=sink), steps, warmup)
+    del buf
+    return ms * 1e3, nbytes // 16 * 16
 
 
 def calibration_copy(mib):
@@ -737,6 +751,16 @@ def main():
             "us": round(ceiling * 1e3, 2), "gbs": round(gbs_ceiling, 2),
             "frac_of_peak": round(gbs_ceiling / HBM_PEAK_GBS, 4),
             "decode_frac_of_achievable": round(gbs_decode / gbs_ceiling, 4),
+        }
+        # the same number of bytes read as a plain streaming read
+        us_sr, nb_sr = streaming_read(kv, K, args.warmup)
+        gbs_sr = nb_sr / (us_sr * 1e-6) / 1e9
+        res["roofline"]["streaming_read"] = {
+            "kernel": "pa_probe_stream: a plain streaming read of a buffer of the same size "
+                      "at its peak launch shape (4 waves per CU, 8 KiB in flight each)",
+            "bytes": nb_sr, "us": round(us_sr, 2), "gbs": round(gbs_sr, 2),
+            "frac_of_peak": round(gbs_sr / HBM_PEAK_GBS, 4),
+            "decode_frac_of_streaming_read": round(gbs_decode / gbs_sr, 4),
         }
     profiled = args.impl == "mfma" and args.partition_size == 0
     traffic, note = measured_traffic(args.kv)

@@ -5,8 +5,9 @@
  * tiles (block 16, head_dim 128) scattered through the pool by the block
  * tables.  The fraction of the HBM peak such a gather can reach depends on
  * the access pattern, not only on the kernel, so the benchmark measures the
- * pattern's own ceiling with the call below and reports pa_decode against
- * it as well as against the 8 TB/s peak.
+ * pattern's own ceiling (pa_probe_gather) and the peak of a plain streaming
+ * read on the same device (pa_probe_stream), and reports pa_decode against
+ * both as well as against the 8 TB/s peak.
  */
 #ifndef PA_PROBE_H
 #define PA_PROBE_H
@@ -35,6 +36,21 @@ pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                           int32_t num_blocks, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Reads `bytes` bytes of `buf` once, as a streaming read: every wave reads
+ * 1 KiB segments (64 lanes x 16 bytes, the streaming hint), segment w, then
+ * w + W, w + 2W, ... for wave w of W, eight in flight, so that the waves
+ * together sweep one contiguous window of memory at a time; one workgroup
+ * of four waves per CU, the shape at which such a read peaks on MI355X
+ * (more bytes in flight per CU read slower).  Computes nothing.  `buf` is a caller-owned device buffer, 16-byte aligned, and
+ * `bytes` a multiple of 16; it is only read.  `sink` as in pa_probe_gather.
+ * Asynchronous on `stream`.  bytes = 0 is a no-op.
+ *
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (misaligned buf, bytes not a multiple
+ * of 16), PA_ERR_HIP.
+ */
+pa_status pa_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

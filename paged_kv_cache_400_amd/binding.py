@@ -45,6 +45,7 @@ SIGNATURES = {
                                       ctypes.c_int, _vp]),
     "pa_probe_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _i32, ctypes.c_int, _vp]),
+    "pa_probe_stream": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "pa_bm_create": (ctypes.c_int, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_num_free": (_i32, [_vp]),
@@ -321,6 +322,19 @@ def probe_gather(k_cache, v_cache, block_tables, seq_lens, num_q_heads, sink=Non
     _check(_lib.pa_probe_gather(_ptr(sink), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                 _ptr(seq_lens), S, num_q_heads, Hkv, d, bs, MB, NB,
                                 _POOL_DT[k_cache.dtype], _stream(dev)))
+    return sink
+
+
+def probe_stream(buf, sink=None):
+    """Measurement support (include/pa_probe.h): read every byte of the
+    device tensor ``buf`` once as a streaming read, computing nothing.
+    Returns the sink tensor (2 int16 words on buf's device)."""
+    _need(buf, "buf", None, None, None)
+    dev = buf.device
+    if sink is None:
+        sink = torch.zeros(2, dtype=torch.int16, device=dev)
+    _check(_lib.pa_probe_stream(_ptr(sink), _ptr(buf), buf.numel() * buf.element_size(),
+                                _stream(dev)))
     return sink
 
 

@@ -8,6 +8,12 @@
 #include "pa_probe.h"
 #include "pa_launch.h"
 
+namespace pa {
+// probe_stream.hip: a streaming read of `bytes` bytes of `buf` (measurement
+// support, outside the decode's launch header).
+hipError_t launch_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t stream);
+}  // namespace pa
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -425,6 +431,19 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                                               dtype == PA_FP8_E4M3 ? 1 : 2, stream);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (bytes == 0) return PA_OK;
+  if (!sink || !buf) return fail(PA_ERR_NULL, "pa_probe_stream: a required pointer is NULL");
+  if (!aligned16(buf) || bytes % 16 != 0)
+    return fail(PA_ERR_SHAPE, "pa_probe_stream: buf must be 16-byte aligned and bytes (%zu) a "
+                "multiple of 16", bytes);
+  const hipError_t e = pa::launch_probe_stream(sink, buf, bytes, stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_probe_stream: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -141,3 +141,13 @@ def test_append_and_copy_reject_bad_arguments(lib):
     assert lib.pa_copy_blocks(P, P, P, 3, 2, 64, 16, 8, 5, NULL) == 3
     assert lib.pa_copy_blocks(P, P, P, 3, 0, 64, 16, 8, 0, NULL) == 2
     assert lib.pa_copy_blocks(NULL, NULL, NULL, 0, 2, 64, 16, 8, 0, NULL) == 0
+
+
+def test_probe_stream_rejects_bad_arguments(lib):
+    P = 1 << 12
+    assert lib.pa_probe_stream(NULL, NULL, 0, NULL) == 0          # nothing to read
+    assert lib.pa_probe_stream(NULL, P, 1 << 20, NULL) == 1
+    assert lib.pa_probe_stream(P, NULL, 1 << 20, NULL) == 1
+    assert lib.pa_probe_stream(P, P + 8, 1 << 20, NULL) == 2      # misaligned
+    assert "aligned" in lib.pa_last_error().decode()
+    assert lib.pa_probe_stream(P, P, 1000, NULL) == 2             # not a multiple of 16

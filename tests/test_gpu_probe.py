@@ -1,6 +1,7 @@
-"""The gather-only measurement call (include/pa_probe.h) runs through the C ABI
-on the benchmark's workload and on edge inputs without touching anything but
-its sink, and rejects bad arguments like pa_decode."""
+"""The measurement calls (include/pa_probe.h) run through the C ABI: the
+gather-only probe on the benchmark's workload and on edge inputs, without
+touching anything but its sink, rejecting bad arguments like pa_decode; the
+streaming read over buffers of several sizes, leaving them unchanged."""
 import pytest
 import torch
 
@@ -31,3 +32,13 @@ def test_probe_gather_rejects_bad_arguments():
     with pytest.raises(pa.PaError, match="group"):
         pa.probe_gather(dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["seq_lens"],
                         b.num_kv_heads * 16)
+
+
+@pytest.mark.parametrize("nbytes", [16, 1008, 1 << 20, (256 << 20) + 48])
+def test_probe_stream_reads_and_writes_nothing_else(nbytes):
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda:0")
+    before = buf.clone()
+    sink = pa.probe_stream(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    assert sink.shape == (2,)
