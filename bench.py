@@ -38,7 +38,8 @@ Prints one JSON line:
               B_kv = sum_s L_s * 2 * Hkv * d * 2 bytes (live K and V read
               once; tail slots of partial blocks not counted)
   roofline    pa_decode's achieved B_kv / (mean duration of its launches,
-              HIP events on its stream over the timed steps) against the
+              HIP events on its stream around each call over K further
+              steps) against the
               8 TB/s HBM peak; `achievable` is the same figure for
               pa_probe_gather, which issues exactly pa_decode's K/V loads and
               computes nothing (the gather pattern's own ceiling);
@@ -136,9 +137,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warmup steps (default 10; 50 with --mode prefill, whose "
-                         "matrix-core kernel runs below full clock for its first ~20 ms, "
-                         "and with --kv fp8, whose first ~10 ms run below full clock too)")
+                    help="untimed warmup steps (default 50: the GPU runs below full clock "
+                         "for the first ~10 ms of decode work and ~20 ms of prefill work)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--ceiling", choices=["on", "off"], default="on",
                     help="also time pa_probe_gather (the same loads, no arithmetic)")
@@ -179,7 +179,7 @@ def parse():
     args = ap.parse_args()
     if args.warmup is None:
         args.warmup = (PREFILL_WARMUP if args.mode == "prefill" else
-                       FP8_WARMUP if args.kv == "fp8" else 10)
+                       FP8_WARMUP if args.kv == "fp8" else DECODE_WARMUP)
     return args
 
 
@@ -250,10 +250,13 @@ def host_block_manager(b, steps=200):
 
 
 def measure(b, dev, args, kv, partition_size, with_ceiling, warmup=None):
-    """Time K steps (append + decode) of batch b after W warmup steps, HIP
-    events on the current stream around the whole run and around each decode
-    call; then, optionally, K gather-only runs.  Returns (ms per step, ms per
-    decode call, ms per gather-only run or None)."""
+    """Time K steps (append + decode) of batch b after W warmup steps: the K
+    steps back to back between two HIP events on the current stream (the
+    step time), then K more with events around each decode call (the call's
+    own duration; an event between two launches costs the stream a few
+    microseconds, so these are not the step time); then, optionally, K
+    gather-only runs.  Returns (ms per step, ms per decode call, ms per
+    gather-only run or None)."""
     import torch
     import paged_kv_cache_400_amd as pa
     S, Hq, d = b.q.shape
@@ -288,19 +291,24 @@ def measure(b, dev, args, kv, partition_size, with_ceiling, warmup=None):
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
         append()
-        ev[i][0].record()
         decode()
-        ev[i][1].record()
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        append()
+        ev[i][0].record()
+        decode()
+        ev[i][1].record()
+    torch.cuda.synchronize()
     ms_decode = sum(a.elapsed_time(z) for a, z in ev) / K
 
     # the access pattern's own ceiling: the same K/V loads, nothing computed
@@ -362,12 +370,16 @@ PREFILL_WARMUP = 50
 # 100 calls averages 198 us, the next ones 190 us); 50 steps are ~10 ms.
 FP8_WARMUP = 50
 
+# Warmup steps of a 16-bit decode measurement, for the same reason: 50 steps
+# are ~17 ms (with 10, the timed steps averaged 349.7 us; with 50, 347.8).
+DECODE_WARMUP = 50
+
 
 def measure_prefill(b, dev, args, warmup=None):
     """K steps of the chunked-prefill step (append of the chunks' keys and
-    values + pa_prefill) after W warmup steps; HIP events on the current
-    stream around the whole run and around each pa_prefill call.  Returns
-    (ms per step, ms per pa_prefill call)."""
+    values + pa_prefill) after W warmup steps, back to back between two HIP
+    events on the current stream; then K more with events around each
+    pa_prefill call.  Returns (ms per step, ms per pa_prefill call)."""
     import torch
     import paged_kv_cache_400_amd as pa
     qs = torch.from_numpy(b.query_start).to("cuda:0")
@@ -386,17 +398,21 @@ def measure_prefill(b, dev, args, warmup=None):
         attend()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
         append()
+        attend()
+    end.record()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        append()
         ev[i][0].record()
         attend()
         ev[i][1].record()
-    end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / K, sum(a.elapsed_time(z) for a, z in ev) / K
 
