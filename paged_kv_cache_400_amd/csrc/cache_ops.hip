@@ -15,24 +15,35 @@
 namespace pa {
 
 // One thread per (token, KV head, 16-byte chunk).  Chunks of one token row
-// are consecutive threads, so a wave writes whole rows.
+// are consecutive threads, so a wave writes whole rows.  The thread's key
+// and value chunks are loaded together with its slot (they do not depend on
+// it): one memory round trip before the stores, not two.  The empty asm
+// takes all three as operands, so that the compiler issues the three loads
+// before it and waits for them once (rather than moving the chunks' loads
+// below the slot test, or waiting for one load before issuing the next).  I is the type of
+// the thread index: 32-bit when the thread count allows (the divisions by
+// the head count and the row's chunk count are then 32-bit ones).
+template <typename I>
 __global__ void __launch_bounds__(256)
 pa_reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
                             uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
-                            const int32_t* __restrict__ slot_mapping, int64_t total,
-                            int32_t hkv, int32_t chunks, int32_t bs, int64_t num_slots) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                            const int32_t* __restrict__ slot_mapping, I total, int32_t hkv,
+                            int32_t chunks, int32_t bs, int64_t num_slots) {
+  const I idx = (I)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int32_t c = (int32_t)(idx % chunks);
-  const int64_t th = idx / chunks;          // token * hkv + head
-  const int32_t h = (int32_t)(th % hkv);
-  const int64_t i = th / hkv;
-  const int64_t slot = slot_mapping[i];
+  const I c = idx % (I)chunks;
+  const I th = idx / (I)chunks;  // token * hkv + head
+  const I h = th % (I)hkv;
+  const I i = th / (I)hkv;
+  uint4 k = key[idx], v = value[idx];
+  int32_t slot = slot_mapping[i];
+  asm volatile("" : "+v"(k.x), "+v"(k.y), "+v"(k.z), "+v"(k.w), "+v"(v.x), "+v"(v.y), "+v"(v.z),
+               "+v"(v.w), "+v"(slot));
   if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
-  const int64_t b = slot / bs, o = slot % bs;
-  const int64_t dst = ((b * hkv + h) * bs + o) * chunks + c;
-  k_cache[dst] = key[idx];
-  v_cache[dst] = value[idx];
+  const int32_t b = slot / bs, o = slot % bs;
+  const int64_t dst = (((int64_t)b * hkv + (int64_t)h) * bs + o) * chunks + (int64_t)c;
+  k_cache[dst] = k;
+  v_cache[dst] = v;
 }
 
 // ---- 8-bit pools ----------------------------------------------------------
@@ -67,26 +78,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
 }
 
 // One thread per (token, KV head, 16 elements): reads 32 bytes of key and of
-// value, writes 16 bytes of codes to each pool.
-template <typename T>
+// value, writes 16 bytes of codes to each pool.  As in the 16-bit append,
+// the rows and the slot are loaded together (the empty asms take them all
+// as operands), and I is the thread index type.
+template <typename T, typename I>
 __global__ void __launch_bounds__(256)
 pa_reshape_and_cache_fp8_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
                                 uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
-                                const int32_t* __restrict__ slot_mapping, int64_t total,
-                                int32_t hkv, int32_t chunks, int32_t bs, int64_t num_slots,
-                                float k_scale, float v_scale) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                const int32_t* __restrict__ slot_mapping, I total, int32_t hkv,
+                                int32_t chunks, int32_t bs, int64_t num_slots, float k_scale,
+                                float v_scale) {
+  const I idx = (I)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int32_t c = (int32_t)(idx % chunks);
-  const int64_t th = idx / chunks;          // token * hkv + head
-  const int32_t h = (int32_t)(th % hkv);
-  const int64_t i = th / hkv;
-  const int64_t slot = slot_mapping[i];
-  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
-  const int64_t b = slot / bs, o = slot % bs;
-  const int64_t dst = ((b * hkv + h) * bs + o) * chunks + c;
-  auto quantise16 = [&](const uint4* src, float scale) {
-    const uint4 x0 = src[2 * idx], x1 = src[2 * idx + 1];
+  const I c = idx % (I)chunks;
+  const I th = idx / (I)chunks;  // token * hkv + head
+  const I h = th % (I)hkv;
+  const I i = th / (I)hkv;
+  uint4 k0 = key[2 * (int64_t)idx], k1 = key[2 * (int64_t)idx + 1];
+  uint4 v0 = value[2 * (int64_t)idx], v1 = value[2 * (int64_t)idx + 1];
+  int32_t slot = slot_mapping[i];
+  asm volatile("" : "+v"(k0.x), "+v"(k0.y), "+v"(k0.z), "+v"(k0.w), "+v"(k1.x), "+v"(k1.y),
+               "+v"(k1.z), "+v"(k1.w), "+v"(slot));
+  asm volatile("" : "+v"(v0.x), "+v"(v0.y), "+v"(v0.z), "+v"(v0.w), "+v"(v1.x), "+v"(v1.y),
+               "+v"(v1.z), "+v"(v1.w));
+  auto quantise16 = [&](const uint4& x0, const uint4& x1, float scale) {
     const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint32_t q[4];
 #pragma unroll
@@ -97,8 +112,13 @@ pa_reshape_and_cache_fp8_kernel(const uint4* __restrict__ key, const uint4* __re
     }
     return make_uint4(q[0], q[1], q[2], q[3]);
   };
-  k_cache[dst] = quantise16(key, k_scale);
-  v_cache[dst] = quantise16(value, v_scale);
+  const uint4 kq = quantise16(k0, k1, k_scale);
+  const uint4 vq = quantise16(v0, v1, v_scale);
+  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
+  const int32_t b = slot / bs, o = slot % bs;
+  const int64_t dst = (((int64_t)b * hkv + (int64_t)h) * bs + o) * chunks + (int64_t)c;
+  k_cache[dst] = kq;
+  v_cache[dst] = vq;
 }
 
 // grid.x = pair; grid.y strides over the block's 16-byte chunks.
@@ -127,10 +147,17 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   const int32_t chunks = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
   const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(pa_reshape_and_cache_kernel, dim3((uint32_t)grid), dim3(256), 0, stream,
-                     (const uint4*)key, (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache,
-                     slot_mapping, total, num_kv_heads, chunks, block_size,
-                     (int64_t)num_blocks * block_size);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (grid * 256 <= (int64_t)UINT32_MAX)
+    hipLaunchKernelGGL(pa_reshape_and_cache_kernel<uint32_t>, dim3((uint32_t)grid), dim3(256), 0,
+                       stream, (const uint4*)key, (const uint4*)value, (uint4*)k_cache,
+                       (uint4*)v_cache, slot_mapping, (uint32_t)total, num_kv_heads, chunks,
+                       block_size, num_slots);
+  else
+    hipLaunchKernelGGL(pa_reshape_and_cache_kernel<int64_t>, dim3((uint32_t)grid), dim3(256), 0,
+                       stream, (const uint4*)key, (const uint4*)value, (uint4*)k_cache,
+                       (uint4*)v_cache, slot_mapping, total, num_kv_heads, chunks, block_size,
+                       num_slots);
   return hipGetLastError();
 }
 
@@ -143,11 +170,21 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
   const int32_t chunks = head_dim / 16;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
   const int64_t grid = (total + 255) / 256;
-  auto kernel = bf16 ? pa_reshape_and_cache_fp8_kernel<BF16> : pa_reshape_and_cache_fp8_kernel<F16>;
-  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(256), 0, stream, (const uint4*)key,
-                     (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, slot_mapping, total,
-                     num_kv_heads, chunks, block_size, (int64_t)num_blocks * block_size, k_scale,
-                     v_scale);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (grid * 256 <= (int64_t)UINT32_MAX) {
+    auto kernel = bf16 ? pa_reshape_and_cache_fp8_kernel<BF16, uint32_t>
+                       : pa_reshape_and_cache_fp8_kernel<F16, uint32_t>;
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(256), 0, stream, (const uint4*)key,
+                       (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, slot_mapping,
+                       (uint32_t)total, num_kv_heads, chunks, block_size, num_slots, k_scale,
+                       v_scale);
+  } else {
+    auto kernel = bf16 ? pa_reshape_and_cache_fp8_kernel<BF16, int64_t>
+                       : pa_reshape_and_cache_fp8_kernel<F16, int64_t>;
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(256), 0, stream, (const uint4*)key,
+                       (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, slot_mapping,
+                       total, num_kv_heads, chunks, block_size, num_slots, k_scale, v_scale);
+  }
   return hipGetLastError();
 }
 
