@@ -143,11 +143,26 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   const int nwh = nwaves / hkv;  // waves per head (the launch has nwaves >= hkv)
   const int kh0 = wave % hkv, jw = wave / hkv;
   if (jw >= nwh) return;
+  // seq_lens is read kLenBatch x 64 lengths at a time, all loads in flight
+  // together: these scans come before the wave's first K/V load, and one
+  // round trip per 64 lengths kept the memory system idle at the start.
+  constexpr int kLenBatch = 4;
+  auto load_lens = [&](int b, int (&Lb)[kLenBatch]) {
+#pragma unroll
+    for (int k = 0; k < kLenBatch; ++k) {
+      const int j = b + 64 * k + lane;
+      Lb[k] = j < num_seqs ? seq_lens[j] : 0;
+    }
+  };
   int64_t per_head = 0, per_head_tiles = 0;  // units and tiles of all sequences
-  for (int b = 0; b < num_seqs; b += 64) {
-    const int L = (b + lane < num_seqs) ? seq_lens[b + lane] : 0;
-    per_head += wave_sum(units_of(L));
-    per_head_tiles += wave_sum(tiles_of(L));
+  for (int b = 0; b < num_seqs; b += 64 * kLenBatch) {
+    int Lb[kLenBatch];
+    load_lens(b, Lb);
+#pragma unroll
+    for (int k = 0; k < kLenBatch; ++k) {
+      per_head += wave_sum(units_of(Lb[k]));
+      per_head_tiles += wave_sum(tiles_of(Lb[k]));
+    }
   }
   const int64_t chunk =
       max((int64_t)(pt == 1 ? kMinChunk : 1), (per_head + nwh - 1) / nwh);  // units per run
@@ -155,26 +170,32 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   if (u0 >= per_head) return;
   const int64_t u1 = min(per_head, u0 + chunk);
 
-  // The sequence holding unit u, where its units start, and where its tiles
-  // start (index of its first unit / tile in the head's order).
-  struct Where { int s; int64_t ustart, tstart; };
+  // The sequence holding unit u, its length, where its units start, and
+  // where its tiles start (index of its first unit / tile in the head's
+  // order).
+  struct Where { int s, L; int64_t ustart, tstart; };
   auto locate = [&](int64_t u) -> Where {
     int64_t urun = 0, trun = 0;
-    for (int b = 0; b < num_seqs; b += 64) {
-      const int L = (b + lane < num_seqs) ? seq_lens[b + lane] : 0;
-      const int un = units_of(L), tn = tiles_of(L);
-      const int uincl = wave_inclusive_scan(un, lane);
-      const int tincl = wave_inclusive_scan(tn, lane);
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(urun + uincl > u);
-      if (hit != 0) {
-        const int i = __builtin_ctzll(hit);
-        return {b + i, urun + lane_value(uincl, i) - lane_value(un, i),
-                trun + lane_value(tincl, i) - lane_value(tn, i)};
+    for (int b = 0; b < num_seqs; b += 64 * kLenBatch) {
+      int Lb[kLenBatch];
+      load_lens(b, Lb);
+#pragma unroll
+      for (int k = 0; k < kLenBatch; ++k) {
+        const int un = units_of(Lb[k]), tn = tiles_of(Lb[k]);
+        const int uincl = wave_inclusive_scan(un, lane);
+        const int tincl = wave_inclusive_scan(tn, lane);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(urun + uincl > u);
+        if (hit != 0) {
+          const int i = __builtin_ctzll(hit);
+          return {b + 64 * k + i, lane_value(Lb[k], i),
+                  urun + lane_value(uincl, i) - lane_value(un, i),
+                  trun + lane_value(tincl, i) - lane_value(tn, i)};
+        }
+        urun += lane_value(uincl, 63);
+        trun += lane_value(tincl, 63);
       }
-      urun += lane_value(uincl, 63);
-      trun += lane_value(tincl, 63);
     }
-    return {-1, urun, trun};
+    return {-1, 0, urun, trun};
   };
   const Where w0 = locate(u0);
   int s = w0.s;
@@ -190,7 +211,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       g1 = w1.tstart + (u1 - w1.ustart) * pt;
     }
   }
-  int L = seq_lens[s];
+  int L = w0.L;
   int ns = tiles_of(L);
   if (ns == 0) return;  // unreachable: the first hit has units
   const int kh = kh0;
