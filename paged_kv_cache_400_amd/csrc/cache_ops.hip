@@ -20,9 +20,10 @@ namespace pa {
 // it): one memory round trip before the stores, not two.  The empty asm
 // takes all three as operands, so that the compiler issues the three loads
 // before it and waits for them once (rather than moving the chunks' loads
-// below the slot test, or waiting for one load before issuing the next).  I is the type of
-// the thread index: 32-bit when the thread count allows (the divisions by
-// the head count and the row's chunk count are then 32-bit ones).
+// below the slot test, or waiting for one load before issuing the next).
+// I is the type of the thread index: 32-bit when the thread count allows
+// (the divisions by the head count and the row's chunk count are then
+// 32-bit ones).
 template <typename I>
 __global__ void __launch_bounds__(256)
 pa_reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
