@@ -183,6 +183,21 @@ def parse():
     return args
 
 
+def host_cpu():
+    """What the CPU baseline ran on: the cores this process may use
+    (sched_getaffinity) and the host CPU's model name (/proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline(b, seconds):
     import oracle
     from paged_kv_cache_400_amd.workload import bits
@@ -212,6 +227,7 @@ def cpu_baseline(b, seconds):
         "value": round(b.kv_bytes() / t / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
+        **host_cpu(),
         "kind": "oracle",
         "sample": (f"the whole step ({len(b.slot_mapping)}-token append + decode of all "
                    f"{b.num_seqs * b.num_q_heads} rows), float64, {reps} repetition(s) of "
@@ -476,7 +492,8 @@ def prefill_line(args):
         fl_sub = prefill_flops(b.seq_lens[:sub], b.query_start[:sub + 1], b.num_q_heads,
                                b.head_dim)
         res["cpu_baseline"] = {"value": round(fl_sub / t / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "cores": oracle.num_threads(), **host_cpu(),
+                               "kind": "oracle",
                                "sample": f"the chunks of the first {sub} sequences ({qe} query "
                                          f"tokens, all heads), float64, one run of {t:.2f} s"}
     return res

@@ -36,7 +36,11 @@
  *     never synchronises.  All array pointers are device pointers.
  *   - Errors: a non-PA_OK status means nothing was enqueued (except
  *     PA_ERR_HIP, a failed launch).  pa_last_error() gives the calling
- *     thread's message for its last failed call.
+ *     thread's message for its last failed call.  Every call checks, before
+ *     launching, that its kernels' LDS fits one workgroup on the current
+ *     device, and answers PA_ERR_UNSUPPORTED if it does not.
+ *   - Device: calls run on the current HIP device; `stream` must belong to
+ *     it.
  *   - Only host-visible arguments are validated.  Device-side contents that
  *     break the contract (a block id outside [0, num_blocks), a sequence
  *     longer than its table, a slot outside the pool) are never
@@ -111,7 +115,9 @@ typedef enum pa_dtype {
  *
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, num_q_heads not a
  * multiple of num_kv_heads, bad partition_size, misaligned pointer),
- * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * PA_ERR_UNSUPPORTED (also when the kernel's LDS or registers do not fit one
+ * workgroup on the current device: nothing is launched), PA_ERR_WORKSPACE,
+ * PA_ERR_HIP.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -136,15 +142,19 @@ pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const vo
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Workspace bytes pa_decode (and pa_decode_valu) need for these sizes; no
- * device memory is read.  The larger of: the balanced split's partial
- * states (two per wave, at most 8192 waves, min(num_q_heads, 8) heads each)
- * and one 16-byte record per (sequence, query head), which pa_decode uses;
- * and the (m, l, acc) per (sequence, query head, partition) of
- * pa_decode_valu's fixed partitions (of partition_size positions, 512 when
- * it is 0), an upper bound from max_blocks_per_seq * block_size that is 0
- * when no sequence can need more than one partition.  0 when an argument is
- * invalid (pa_decode then reports the error).
+ * Workspace bytes pa_decode (and pa_decode_valu) need for these sizes on the
+ * current device; no device memory is read.  The larger of: the balanced
+ * split's partial states, two per wave of the launch (two workgroups of four
+ * waves per CU of the current device: 2048 waves on a 256-CU MI355X; at
+ * most 8192, and 8192 when no device can be queried), min(num_q_heads, 8)
+ * heads of head_dim floats plus (m, l) each, and one 16-byte record per
+ * (sequence, query head), which pa_decode uses; and the (m, l, acc) per
+ * (sequence, query head, partition) of pa_decode_valu's fixed partitions (of
+ * partition_size positions, 512 when it is 0), an upper bound from
+ * max_blocks_per_seq * block_size that is 0 when no sequence can need more
+ * than one partition.  0 when an argument is invalid (pa_decode then
+ * reports the error).  A workspace sized on one device serves calls on any
+ * device with as many CUs or fewer.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_blocks_per_seq, int32_t block_size,

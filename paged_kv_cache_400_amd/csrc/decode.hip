@@ -58,6 +58,9 @@ pa_decode_valu(uint16_t* __restrict__ out, float* __restrict__ ws_acc, float2* _
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ int s_bad;
+  static_assert(sizeof(s_bt) + sizeof(s_acc) + sizeof(s_m) + sizeof(s_l) + sizeof(s_bad) <=
+                    kMaxLdsBytes,
+                "one workgroup's LDS fits gfx950's 160 KiB");
 
   const Unit u = unit_of(blockIdx.x, hkv, pmax);
   const int s = u.s, kh = u.kh, p = u.p;
@@ -321,6 +324,9 @@ hipError_t launch_splitk_reduce(const DecodeArgs& a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BS, int G>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
+  static int lds_cache[kMaxDevices];
+  const hipError_t fit = check_lds((const void*)pa_decode_valu<T, D, BS, G>, 0, lds_cache);
+  if (fit != hipSuccess) return fit;
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.pmax;
   hipLaunchKernelGGL((pa_decode_valu<T, D, BS, G>), dim3((uint32_t)units), dim3(kThreads), 0,
                      a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, (const uint16_t*)a.q,

@@ -62,6 +62,16 @@ constexpr int kWaves = 4;              // waves per workgroup (independent)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMinChunk = 8;           // tiles per wave at least
 
+// Workgroups per CU the launch uses: two (8 waves), not the three that fit.
+// The K/V gather saturates with as few as 4 waves per CU (the gather-only
+// probe takes the same time with 4 to 20), so the third workgroup adds no
+// loads in flight that the memory system can use; it only makes the runs a
+// third shorter (more pairs cut, more partials, more wave starts) and puts
+// a third more waves on each SIMD.  Measured with two instead of three:
+// mixed decode step 358 -> 346 us, the same over 8-bit pools 222 -> 204 us,
+// long context at block 16 416 -> 394 us.
+constexpr int kWorkgroupsPerCu = 2;
+
 // Sum over the wave, returned as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -120,6 +130,9 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   constexpr int KL = TW::KL, NM = TW::NM, kT = TW::kTileLen, kIds = TW::kIds;
   constexpr bool kScaled = !std::is_same<KV, T>::value;
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * TW::kTileBytes];
+  static_assert(sizeof(s_mem) <= kMaxLdsBytes, "one workgroup's LDS fits gfx950's 160 KiB");
+  static_assert(kWorkgroupsPerCu * sizeof(s_mem) <= kMaxLdsBytes,
+                "the workgroups the launch puts on one CU fit its LDS together");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -430,50 +443,58 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
 }
 
 // ---------------------------------------------------------------------------
-// Workgroups per CU the launch uses: two (8 waves), not the three that fit.
-// The K/V gather saturates with as few as 4 waves per CU (the gather-only
-// probe takes the same time with 4 to 20), so the third workgroup adds no
-// loads in flight that the memory system can use; it only makes the runs a
-// third shorter (more pairs cut, more partials, more wave starts) and puts
-// a third more waves on each SIMD.  Measured with two instead of three:
-// mixed decode step 358 -> 346 us, the same over 8-bit pools 222 -> 204 us,
-// long context at block 16 416 -> 394 us.
-constexpr int kWorkgroupsPerCu = 2;
 
 // Waves of one decode launch on the current device: kWorkgroupsPerCu
-// workgroups per CU, or fewer if fewer fit (cached per instantiation and
-// device; recomputing it gives the same value, so concurrent first calls are
-// harmless).
+// workgroups per CU, or fewer if fewer fit; kErrDoesNotFit if not one
+// workgroup fits a CU or its LDS exceeds the device's per-workgroup limit
+// (cached per instantiation and device; recomputing gives the same answer,
+// so concurrent first calls are harmless).
 template <typename T, typename KV, int D, int BS, int G>
-static int launch_waves() {
-  constexpr int kMaxDevices = 64;
-  static int cache[kMaxDevices];
+static hipError_t launch_waves(int* waves) {
+  static int cache[kMaxDevices];  // > 0 waves, -1 does not fit, 0 unknown
+  static int lds_cache[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int cached = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-  if (cached > 0) return cached;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int cached = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (cached != 0) {
+    *waves = cached;
+    return cached > 0 ? hipSuccess : kErrDoesNotFit;
+  }
+  auto kernel = pa_decode_streamk<T, D, BS, G, false, KV>;
+  e = check_lds((const void*)kernel, 0, lds_cache);
+  if (e != hipSuccess && e != kErrDoesNotFit) return e;
   int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, pa_decode_streamk<T, D, BS, G, false, KV>, kThreads, 0) != hipSuccess)
-    return 0;
-  const int waves = cus * max(min(per_cu, kWorkgroupsPerCu), 1) * kWaves;
-  __atomic_store_n(&cache[dev], waves, __ATOMIC_RELAXED);
-  return waves;
+  if (e == hipSuccess) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+  }
+  const int n = (per_cu > 0 && cus > 0) ? cus * min(per_cu, kWorkgroupsPerCu) * kWaves : -1;
+  __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  *waves = n;
+  return n > 0 ? hipSuccess : kErrDoesNotFit;
 }
 
 template <typename T, typename KV, int D, int BS, int G>
 static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
-  int waves = launch_waves<T, KV, D, BS, G>();
-  if (waves <= 0) return hipErrorInvalidDevice;
-  if (a.num_kv_heads > kStreamKMaxWaves) return hipErrorInvalidValue;
-  // a whole number of waves per KV head, at least one
-  waves = max(min(waves, kStreamKMaxWaves) / a.num_kv_heads, 1) * a.num_kv_heads;
+  int waves = 0;
+  hipError_t e = launch_waves<T, KV, D, BS, G>(&waves);
+  if (e != hipSuccess) return e;
+  // no more waves than the workspace holds partial slots for, a whole
+  // number per KV head, at least one
+  const int cap = gather ? kStreamKMaxWaves : min(a.max_waves, kStreamKMaxWaves);
+  if (a.num_kv_heads > cap) return hipErrorInvalidValue;
+  waves = max(min(waves, cap) / a.num_kv_heads, 1) * a.num_kv_heads;
   if (gather) {  // the same grid, gather-only (the group does not change the loads)
-    hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, 1, true, KV>),
-                       dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
+    static int lds_cache[kMaxDevices];
+    auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV>;
+    e = check_lds((const void*)kernel, 0, lds_cache);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
                        dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
                        nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                        a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
@@ -487,7 +508,7 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                      a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
                      a.max_blocks_per_seq, a.num_blocks, waves, a.part_tiles, a.qk_scale,
                      a.out_scale);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pa_streamk_reduce<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),
                      dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,

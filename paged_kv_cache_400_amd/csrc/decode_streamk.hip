@@ -13,4 +13,13 @@ hipError_t launch_gather_streamk(const StreamKArgs& a) {
   return a.bf16 ? launch_d<BF16, BF16>(a, true) : launch_d<F16, F16>(a, true);
 }
 
+int streamk_device_waves() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return kStreamKMaxWaves;
+  return (int)min((int64_t)cus * kWorkgroupsPerCu * kWaves, (int64_t)kStreamKMaxWaves);
+}
+
 }  // namespace pa

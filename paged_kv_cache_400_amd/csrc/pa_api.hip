@@ -28,6 +28,18 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Status of a launcher's result: a kernel whose resources do not fit the
+// device (pa::kErrDoesNotFit) is PA_ERR_UNSUPPORTED, any other failure
+// PA_ERR_HIP.
+pa_status launch_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (e == pa::kErrDoesNotFit)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: the kernel's LDS or register needs do not fit one workgroup on this device",
+                fn);
+  return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+}
+
 constexpr int32_t kAutoPartition = 512;
 constexpr int64_t kMaxThreadsPerLaunch = (int64_t)1 << 32;
 
@@ -98,7 +110,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   // pa_decode runs the balanced kernel (partition-aligned runs when
   // partition_size > 0), pa_decode_valu fixed partitions (512 positions when
   // partition_size is 0); the workspace serves either
-  const size_t sk = (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim);
+  const size_t sk = (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                        pa::streamk_device_waves());
   return sk > part_bytes ? sk : part_bytes;
 }
 
@@ -159,8 +172,9 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     return fail(PA_ERR_SHAPE, "pa_decode: %lld work units exceed one launch",
                 (long long)units);
   const bool balanced = impl == Impl::kMfma;
+  const int waves = pa::streamk_device_waves();
   const size_t need =
-      balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim)
+      balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim, waves)
                : partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                                              block_size, partition_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -179,9 +193,10 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     a.seq_lens = seq_lens;
     char* ws = (char*)workspace;
     a.ws_acc = (float*)ws;
-    a.ws_ml = (float2*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim));
-    a.ws_meta = (int4*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim) +
-                        pa::streamk_ml_bytes(num_q_heads));
+    a.ws_ml = (float2*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim, waves));
+    a.ws_meta = (int4*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim, waves) +
+                        pa::streamk_ml_bytes(num_q_heads, waves));
+    a.max_waves = waves;
     a.num_seqs = num_seqs;
     a.num_kv_heads = num_kv_heads;
     a.group = group;
@@ -194,10 +209,8 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     a.out_scale = v_scale;
     a.bf16 = dtype == PA_BF16;
     a.stream = stream;
-    const hipError_t e = kv_fp8 ? pa::launch_decode_streamk_fp8(a) : pa::launch_decode_streamk(a);
-    if (e != hipSuccess)
-      return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
-    return PA_OK;
+    return launch_status(kv_fp8 ? "pa_decode_fp8" : "pa_decode",
+                         kv_fp8 ? pa::launch_decode_streamk_fp8(a) : pa::launch_decode_streamk(a));
   }
 
   pa::DecodeArgs a;
@@ -222,10 +235,7 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
   a.qk_scale = scale * 1.4426950408889634f;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = pa::launch_decode(a);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_status("pa_decode_valu", pa::launch_decode(a));
 }
 
 }  // namespace
@@ -300,13 +310,11 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
   const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 16);
   if (total + 255 >= kMaxThreadsPerLaunch)
     return fail(PA_ERR_SHAPE, "pa_reshape_and_cache_fp8: too many tokens for one launch");
-  const hipError_t e = pa::launch_reshape_and_cache_fp8(
-      key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
-      num_blocks, k_scale, v_scale, dtype == PA_BF16, stream);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_reshape_and_cache_fp8: launch failed: %s",
-                hipGetErrorString(e));
-  return PA_OK;
+  return launch_status("pa_reshape_and_cache_fp8",
+                       pa::launch_reshape_and_cache_fp8(
+                           key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                           head_dim, block_size, num_blocks, k_scale, v_scale, dtype == PA_BF16,
+                           stream));
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -362,10 +370,7 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
   a.qk_scale = scale * 1.4426950408889634f;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = pa::launch_prefill(a);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_prefill: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_status("pa_prefill", pa::launch_prefill(a));
 }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
@@ -394,12 +399,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
   if (total + 255 >= kMaxThreadsPerLaunch)
     return fail(PA_ERR_SHAPE, "pa_reshape_and_cache: too many tokens for one launch");
-  const hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+  return launch_status("pa_reshape_and_cache",
+                       pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
                                                     num_tokens, num_kv_heads, head_dim,
-                                                    block_size, num_blocks, stream);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_reshape_and_cache: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+                                                    block_size, num_blocks, stream));
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
@@ -426,12 +429,10 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
     return fail(PA_ERR_NULL, "pa_copy_blocks: a required pointer is NULL");
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: pools must be 16-byte aligned");
-  const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
+  return launch_status("pa_copy_blocks",
+                       pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
                                               num_kv_heads, head_dim, block_size, num_blocks,
-                                              dtype == PA_FP8_E4M3 ? 1 : 2, stream);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+                                              dtype == PA_FP8_E4M3 ? 1 : 2, stream));
 }
 
 pa_status pa_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t stream) {
@@ -441,10 +442,7 @@ pa_status pa_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t
   if (!aligned16(buf) || bytes % 16 != 0)
     return fail(PA_ERR_SHAPE, "pa_probe_stream: buf must be 16-byte aligned and bytes (%zu) a "
                 "multiple of 16", bytes);
-  const hipError_t e = pa::launch_probe_stream(sink, buf, bytes, stream);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_probe_stream: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_status("pa_probe_stream", pa::launch_probe_stream(sink, buf, bytes, stream));
 }
 
 pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
@@ -489,11 +487,9 @@ pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
   a.num_blocks = num_blocks;
   a.bf16 = dtype == PA_BF16;
   a.stream = stream;
-  const hipError_t e = dtype == PA_FP8_E4M3 ? pa::launch_gather_streamk_fp8(a)
-                                            : pa::launch_gather_streamk(a);
-  if (e != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_probe_gather: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_status("pa_probe_gather", dtype == PA_FP8_E4M3
+                                                ? pa::launch_gather_streamk_fp8(a)
+                                                : pa::launch_gather_streamk(a));
 }
 
 }  // extern "C"

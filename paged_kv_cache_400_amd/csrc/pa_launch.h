@@ -7,6 +7,48 @@
 
 namespace pa {
 
+// ---- LDS limits -----------------------------------------------------------
+// gfx950 gives one workgroup at most 160 KiB of LDS.  Every kernel checks its
+// static LDS against this at compile time (static_assert beside its
+// __shared__ arrays); the launchers also check the kernel's LDS against the
+// device's own per-workgroup limit before launching, because a launch whose
+// workgroup needs more LDS than the device has is accepted by the runtime and
+// then aborts the queue (HSA_STATUS_ERROR_INVALID_ALLOCATION), taking the
+// process's later GPU work with it.
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+// What a launcher returns when its kernel cannot be launched on the current
+// device because of its resources (LDS, or no workgroup fits a CU); the C
+// ABI reports it as PA_ERR_UNSUPPORTED.
+constexpr hipError_t kErrDoesNotFit = hipErrorInvalidConfiguration;
+
+constexpr int kMaxDevices = 64;
+
+// hipSuccess if `kernel` (its static LDS plus `dynamic_bytes`) fits one
+// workgroup on the current device, kErrDoesNotFit if not, another error if
+// the runtime cannot tell.  `cache` is the caller's per-device memo (one per
+// kernel instantiation): 1 fits, -1 does not, 0 not yet known; recomputing
+// gives the same answer, so concurrent first calls are harmless.
+inline hipError_t check_lds(const void* kernel, size_t dynamic_bytes,
+                            int (&cache)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int known = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (known != 0) return known > 0 ? hipSuccess : kErrDoesNotFit;
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, kernel);
+  if (e != hipSuccess) return e;
+  int limit = 0;
+  e = hipDeviceGetAttribute(&limit, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  const bool fits = attr.sharedSizeBytes + dynamic_bytes <= (size_t)limit &&
+                    attr.sharedSizeBytes + dynamic_bytes <= (size_t)kMaxLdsBytes;
+  __atomic_store_n(&cache[dev], fits ? 1 : -1, __ATOMIC_RELAXED);
+  return fits ? hipSuccess : kErrDoesNotFit;
+}
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -24,9 +66,10 @@ struct DecodeArgs {
 };
 
 // Balanced (stream-K) decode (decode_streamk.hip), pa_decode's automatic
-// mode.  Workspace: ws_acc float [2 * kStreamKMaxWaves][Gmax][D], then ws_ml
-// float2 [2 * kStreamKMaxWaves][Gmax], then ws_meta int4 [S * Hkv], with
-// Gmax = min(Hq, 8); streamk_workspace_bytes gives the total.
+// mode.  Workspace, for a launch of W waves: ws_acc float [2 * W][Gmax][D],
+// then ws_ml float2 [2 * W][Gmax], then ws_meta int4 [S * Hq] (one record
+// per (sequence, KV head) is used), with Gmax = min(Hq, 8);
+// streamk_workspace_bytes gives the total.  W is at most kStreamKMaxWaves.
 constexpr int kStreamKMaxWaves = 8192;
 
 struct StreamKArgs {
@@ -39,6 +82,7 @@ struct StreamKArgs {
   float* ws_acc;
   float2* ws_ml;
   int4* ws_meta;
+  int32_t max_waves;  // waves the workspace holds partial slots for
   int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
   int32_t max_blocks_per_seq, num_blocks;
   int32_t part_tiles; // 0: runs cut at any tile; else only at multiples of this many tiles
@@ -48,16 +92,25 @@ struct StreamKArgs {
   hipStream_t stream;
 };
 
+// Waves a balanced decode launch has on the current device (two workgroups
+// of four waves per CU), at most kStreamKMaxWaves; kStreamKMaxWaves when no
+// device can be queried.
+int streamk_device_waves();
+
 inline int64_t streamk_gmax(int32_t num_q_heads) { return num_q_heads < 8 ? num_q_heads : 8; }
-inline int64_t streamk_acc_bytes(int32_t num_q_heads, int32_t head_dim) {
-  return 2 * (int64_t)kStreamKMaxWaves * streamk_gmax(num_q_heads) * head_dim * 4;
+inline int64_t streamk_acc_bytes(int32_t num_q_heads, int32_t head_dim, int64_t waves) {
+  return 2 * waves * streamk_gmax(num_q_heads) * head_dim * 4;
 }
-inline int64_t streamk_ml_bytes(int32_t num_q_heads) {
-  return 2 * (int64_t)kStreamKMaxWaves * streamk_gmax(num_q_heads) * 8;
+inline int64_t streamk_ml_bytes(int32_t num_q_heads, int64_t waves) {
+  return 2 * waves * streamk_gmax(num_q_heads) * 8;
 }
-inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
-  return streamk_acc_bytes(num_q_heads, head_dim) + streamk_ml_bytes(num_q_heads) +
-         (int64_t)num_seqs * num_q_heads * 16;
+inline int64_t streamk_meta_bytes(int32_t num_seqs, int32_t num_q_heads) {
+  return (int64_t)num_seqs * num_q_heads * 16;
+}
+inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int64_t waves) {
+  return streamk_acc_bytes(num_q_heads, head_dim, waves) + streamk_ml_bytes(num_q_heads, waves) +
+         streamk_meta_bytes(num_seqs, num_q_heads);
 }
 
 hipError_t launch_decode_streamk(const StreamKArgs& a);

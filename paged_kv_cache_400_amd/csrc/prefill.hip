@@ -196,6 +196,8 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
   static_assert(kRows % G == 0, "whole tokens per row block");
   __shared__ __attribute__((aligned(16))) unsigned char s_st0[SG::BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char s_st1[SG::BYTES];
+  static_assert(sizeof(s_st0) + sizeof(s_st1) <= kMaxLdsBytes,
+                "one workgroup's LDS fits gfx950's 160 KiB");
   unsigned char* const s_mem = s_st0;
   static_assert(sizeof(float) * kRows * D <= 2 * SG::BYTES / kWaves,
                 "a row block's result fits the wave's quarter of the LDS");
@@ -590,6 +592,9 @@ static int64_t units_per_xcd(int32_t total_q, int32_t num_seqs, int32_t hkv, int
 
 template <typename T, int D, int BS, int G>
 static hipError_t launch_t(const PrefillArgs& a) {
+  static int lds_cache[kMaxDevices];
+  const hipError_t fit = check_lds((const void*)pa_prefill_kernel<T, D, BS, G>, 0, lds_cache);
+  if (fit != hipSuccess) return fit;
   const int64_t grid = 8 * units_per_xcd(a.total_q, a.num_seqs, a.num_kv_heads, G);
   hipLaunchKernelGGL((pa_prefill_kernel<T, D, BS, G>), dim3((uint32_t)grid), dim3(kThreads), 0,
                      a.stream, (uint16_t*)a.out, (const uint16_t*)a.q,

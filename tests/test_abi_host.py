@@ -70,11 +70,17 @@ def test_one_hip_runtime_is_mapped(lib):
 def test_workspace_bytes(lib):
     f = lib.pa_decode_workspace_bytes
 
-    # pa_decode's balanced split: two partial slots per wave (at most 8192
-    # waves, min(Hq, 8) heads of d floats + (m, l) each) and one 16-byte
-    # record per (sequence, query head), with or without partition_size
+    # pa_decode's balanced split: two partial slots per wave of the launch
+    # (two workgroups of four waves per CU of the current device, at most
+    # 8192; 8192 with no device), min(Hq, 8) heads of d floats + (m, l) each,
+    # and one 16-byte record per (sequence, query head), with or without
+    # partition_size
+    waves = 8192
+    if torch.cuda.is_available():
+        waves = min(8192, 8 * torch.cuda.get_device_properties(0).multi_processor_count)
+
     def balanced(S, Hq, d):
-        return 2 * 8192 * min(Hq, 8) * (d * 4 + 8) + S * Hq * 16
+        return 2 * waves * min(Hq, 8) * (d * 4 + 8) + S * Hq * 16
 
     # pa_decode_valu's fixed partitions: (m, l, acc) per (sequence, query head,
     # partition); the larger of the two is returned
