@@ -92,9 +92,11 @@ typedef enum pa_dtype {
  * h / (num_q_heads / num_kv_heads), L_s = seq_lens[s].  L_s = 0 gives a
  * zero row.  Slots at positions >= L_s and table entries past
  * ceil(L_s / block_size) are never read (they may hold anything, NaN
- * included).  Scores, softmax and sums are float32; the softmax weights are
- * rounded to `dtype` for the P.V product (the denominator sums the rounded
- * weights); out is rounded to `dtype` (round to nearest even).
+ * included).  Scores, softmax and sums are float32; each softmax weight
+ * enters the P.V product as two `dtype` values, hi = round(p) and lo =
+ * round(p - hi), whose sum is p to 2^-16 of p (bf16; 2^-22 for fp16), so
+ * the result's error does not grow with |V|; the denominator sums the
+ * float32 weights; out is rounded to `dtype` (round to nearest even).
  *
  * Supported: dtype F16/BF16 (q, pools and out share it); head_dim 64 or
  * 128; block_size 8, 16 or 32; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
@@ -132,7 +134,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * row, P.V as float32 FMAs.  Same arguments, contract, workspace and errors
  * as pa_decode, except that partition_size = 0 means fixed 512-position
  * partitions; results agree to rounding (the two sum in different orders,
- * and this kernel keeps P in float32).
+ * and this kernel keeps P in float32).  Unlike pa_decode, its result for a
+ * sequence does not depend on the other sequences of the batch, bit for
+ * bit: every (sequence, KV head, partition) is one workgroup's fixed-order
+ * computation, merged in partition order.
  */
 pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -204,8 +209,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
  * pa_decode_fp8: pa_decode over 8-bit pools, always with the balanced split
  * (tiles of 32 positions).  q and out are `dtype` (PA_F16 or PA_BF16); keys
  * and values are widened exactly to `dtype` for the products; scores,
- * softmax and sums are float32 as in pa_decode (the softmax weights rounded
- * to `dtype` for the P.V product).  Workspace: pa_decode_workspace_bytes(
+ * softmax and sums are float32 as in pa_decode (each softmax weight split
+ * into a hi and a lo `dtype` part for the P.V product).  Workspace:
+ * pa_decode_workspace_bytes(
  * num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, 0).  Same
  * supported sizes, contract for unused slots and table entries, NaN rows for
  * contract violations, and errors as pa_decode; k_scale and v_scale must be
@@ -255,8 +261,12 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
  * num_kv_heads).  n_s = 1 is decode; n_s = L_s is a whole prompt; n_s = 0
  * writes nothing.  q and out are [total_q][num_q_heads][head_dim];
  * query_start holds num_seqs + 1 non-decreasing offsets from 0 to total_q
- * (device memory).  Arithmetic as pa_decode (float32 scores and sums,
- * softmax weights rounded to dtype for P.V, out rounded to dtype).
+ * (device memory).  Arithmetic: float32 scores and sums; unlike pa_decode,
+ * each softmax weight is rounded once to dtype for P.V (this kernel is
+ * bound by the matrix cores, and the split would double its P.V work) and
+ * the denominator sums the same rounded weights, so a weight errs by up to
+ * 2^-8 of itself (bf16; 2^-11 for fp16) and the result by up to that
+ * fraction of max_t |V_t - out|; out rounded to dtype.
  *
  * Supported: dtype F16/BF16; head_dim 64 or 128; block_size 8, 16 or 32;
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}.  No workspace.

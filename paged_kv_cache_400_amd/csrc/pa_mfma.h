@@ -20,15 +20,23 @@
 //          a head is raised only when a score exceeds it by more than 8
 //          (then every weight stays <= 2^8); that test is a wave-wide
 //          ballot, so the usual tile needs no lane exchange and no rescale.
-//  P.V     acc[h][d] += sum_t P[h][t] V[t][d] as D/16 v_mfma_f32_16x16x16
-//          (A = P: the q.K^T result is already in the A layout; B = V with
-//          the 16 positions along k).  The V tile is stored as four 4-row
-//          regions, each padded by 32 bytes; lane group g's B operand (rows
-//          4g..4g+3 of column 16 m + col) is one LDS transpose read
-//          (ds_read_b64_tr_b16) from region g.
-//  P is rounded to the input type for the P.V product and the softmax
-//  denominator sums the same rounded weights.  MFMA rows for heads >= G
-//  compute on zero queries and are never written.
+//  P.V     acc[h][d] += sum_t P[h][t] V[t][d] as D/16 v_mfma_f32_16x16x32.
+//          Each float32 weight p is split into two values of the input
+//          type, hi = round(p) and lo = round(p - hi), so hi + lo equals p
+//          to 2^-16 of p (bf16; 2^-22 for fp16) instead of the 2^-8 one
+//          rounding leaves (bf16), which would err in proportion to |V|.  The
+//          32-long k axis of the MFMA holds the 16 positions twice: lane
+//          group g's 8 k-values are (hi of positions 4g..4g+3, lo of the
+//          same), and the V operand is the same 4 rows twice, so
+//          sum_k A B = sum_t (hi_t + lo_t) V_t.  On gfx950 the 16x16x32 form
+//          issues at the rate of the 16x16x16 one, so the split costs no
+//          matrix-core time.  A = the weights, straight from the q.K^T
+//          result's layout; the V tile is stored as four 4-row regions,
+//          each padded by 32 bytes, and lane group g's 4 rows of column
+//          16 m + col are one LDS transpose read (ds_read_b64_tr_b16) from
+//          region g.
+//  The softmax denominator sums the float32 weights.  MFMA rows for heads
+//  >= G compute on zero queries and are never written.
 #pragma once
 
 #include "pa_device.h"
@@ -56,16 +64,6 @@ template <> __device__ __forceinline__ f32x4_t mfma_k32<F16>(uint4 a, uint4 b, f
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-template <typename T> __device__ __forceinline__ f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c);
-template <> __device__ __forceinline__ f32x4_t mfma_k16<BF16>(uint2 a, uint2 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
-}
-template <> __device__ __forceinline__ f32x4_t mfma_k16<F16>(uint2 a, uint2 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                               __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
-}
-
 // Two floats -> two 16-bit values packed in one word (round to nearest even).
 template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
 template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
@@ -73,6 +71,17 @@ template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) 
 }
 template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+}
+
+// Four float32 softmax weights as the k-values of a 16x16x32 P.V product:
+// (hi of w0..w3, lo of w0..w3), hi = w rounded to T, lo = (w - hi) rounded
+// to T; hi + lo is w to 2^-16 of w for bf16 (2^-22 for fp16, down to the
+// fp16 subnormal spacing for weights below 2^-2).
+template <typename T> __device__ __forceinline__ uint4 split_weights(const float (&w)[4]) {
+  const uint32_t h01 = pack2<T>(w[0], w[1]), h23 = pack2<T>(w[2], w[3]);
+  const uint32_t l01 = pack2<T>(w[0] - lo_f32<T>(h01), w[1] - hi_f32<T>(h01));
+  const uint32_t l23 = pack2<T>(w[2] - lo_f32<T>(h23), w[3] - hi_f32<T>(h23));
+  return make_uint4(h01, h23, l01, l23);
 }
 
 // s_waitcnt vmcnt(0): every outstanding vector-memory load of this wave,
@@ -223,23 +232,25 @@ struct TileWave {
         for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
       }
     }
-    const uint32_t p01 = pack2<T>(exp2_fast(sr[0] - m_run), exp2_fast(sr[1] - m_run));
-    const uint32_t p23 = pack2<T>(exp2_fast(sr[2] - m_run), exp2_fast(sr[3] - m_run));
-    l_run += (lo_f32<T>(p01) + hi_f32<T>(p01)) + (lo_f32<T>(p23) + hi_f32<T>(p23));
-    const uint2 pa_op = make_uint2(p01, p23);
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = exp2_fast(sr[r] - m_run);
+    l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    const uint4 pa_op = split_weights<T>(pw);
 
-    // B operand: V[4*grp + r][16*m + col] from region grp, row r.
-    // ds_read_b64_tr_b16 transposes within each group of 16 lanes: lanes
-    // 4r .. 4r + 3 give row r (columns 16 m .. 16 m + 15, 4 each) and lane
-    // col receives element col of every row.
+    // B operand: V[4*grp + r][16*m + col] from region grp, row r, given
+    // twice (for the hi and the lo weights).  ds_read_b64_tr_b16 transposes
+    // within each group of 16 lanes: lanes 4r .. 4r + 3 give row r (columns
+    // 16 m .. 16 m + 15, 4 each) and lane col receives element col of every
+    // row.
     typedef short i16x4_t2 __attribute__((ext_vector_type(4)));
     const unsigned char* vb = vtile + buf * GE::TILE + grp * GE::REGION + (col >> 2) * GE::ROW +
                               8 * (col & 3);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const i16x4_t2 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t2*)(vb + 32 * m));
-      acc[m] = mfma_k16<T>(pa_op, __builtin_bit_cast(uint2, w), acc[m]);
+      const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t2*)(vb + 32 * m)));
+      acc[m] = mfma_k32<T>(pa_op, make_uint4(w.x, w.y, w.x, w.y), acc[m]);
     }
   }
 

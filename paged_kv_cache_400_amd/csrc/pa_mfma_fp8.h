@@ -27,14 +27,19 @@
 //          16*grp + 0..7 and the second for + 8..15; q is held in the same
 //          d order.  Lane l receives head l%16's scores for positions
 //          4*(l/16) + r of each half.
-//  P.V     D/16 v_mfma_f32_16x16x32 with the 32 positions on k in the order
-//          (half 0: 4*grp + 0..3, half 1: 4*grp + 0..3) for lane group grp:
-//          that is exactly what the lane holds of P after q.K^T, and exactly
-//          the 8 rows of region grp of the V tile.  The B operand of MFMA m
-//          (the 8 rows' bytes of column 16 m + col) is one LDS transpose read
-//          (ds_read_b64_tr_b8) widened to 16 bits.  Reading it byte by byte
-//          instead costs 64 LDS reads per tile and 10% of the mixed decode
-//          step; reading whole rows and transposing in registers, 3%.
+//  P.V     2 D/16 v_mfma_f32_16x16x32 with the 32 positions on k in the
+//          order (half 0: 4*grp + 0..3, half 1: 4*grp + 0..3) for lane group
+//          grp: that is exactly what the lane holds of P after q.K^T, and
+//          exactly the 8 rows of region grp of the V tile.  Each float32
+//          weight is split as in TileWave into hi = round(p) and lo =
+//          round(p - hi), one MFMA per part against the same V operand, so
+//          the weights err by 2^-16 of p (bf16) and not by the 2^-8 a single
+//          rounding leaves, which would err in proportion to |V|.  The B
+//          operand of MFMA m (the 8 rows' bytes of column 16 m + col) is one
+//          LDS transpose read (ds_read_b64_tr_b8) widened to 16 bits.
+//          Reading it byte by byte instead costs 64 LDS reads per tile and
+//          10% of the mixed decode step; reading whole rows and transposing
+//          in registers, 3%.  The denominator sums the float32 weights.
 #pragma once
 
 #include "pa_mfma.h"
@@ -208,13 +213,18 @@ struct TileWave8 {
         for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
       }
     }
-    uint32_t p[4];
+    float pw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pw[j] = exp2_fast(sr[j] - m_run);
+    l_run += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+    uint32_t ph[4], pl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p[j] = pack2<T>(exp2_fast(sr[2 * j] - m_run), exp2_fast(sr[2 * j + 1] - m_run));
-      l_run += lo_f32<T>(p[j]) + hi_f32<T>(p[j]);
+      ph[j] = pack2<T>(pw[2 * j], pw[2 * j + 1]);
+      pl[j] = pack2<T>(pw[2 * j] - lo_f32<T>(ph[j]), pw[2 * j + 1] - hi_f32<T>(ph[j]));
     }
-    const uint4 pa_op = make_uint4(p[0], p[1], p[2], p[3]);
+    const uint4 pa_hi = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    const uint4 pa_lo = make_uint4(pl[0], pl[1], pl[2], pl[3]);
 
     // B operand of MFMA m: V[row j of region grp][16 m + col], j = 0..7.
     // ds_read_b64_tr_b8 transposes within each group of 16 lanes: lanes 2j
@@ -227,7 +237,9 @@ struct TileWave8 {
     for (int m = 0; m < NM; ++m) {
       const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
           (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * m));
-      acc[m] = mfma_k32<T>(pa_op, widen8<T>((uint32_t)w.x, (uint32_t)w.y), acc[m]);
+      const uint4 vop = widen8<T>((uint32_t)w.x, (uint32_t)w.y);
+      acc[m] = mfma_k32<T>(pa_hi, vop, acc[m]);
+      acc[m] = mfma_k32<T>(pa_lo, vop, acc[m]);
     }
   }
 

@@ -38,7 +38,8 @@ entries past a sequence's last block point at a never-allocated NaN block.
 8-bit pools (``kv="fp8"``) hold OCP E4M3 codes drawn directly, not made from
 values (no quantising happens here): a uniform sign bit and a magnitude code
 uniform in 0x00..0x77 (0 to 240), i.e. values up to 3.75 at the default
-scale 2^-6; slots that hold no token hold the NaN code 0x7F.  The appended
+scale 2^-6, or up to any code through 0x7E (448) on request; slots that hold
+no token hold the NaN code 0x7F.  The appended
 tokens' rows stay 16-bit N(0, 1) values, which the step's append quantises.
 """
 import math
@@ -137,20 +138,21 @@ def _place(pool: torch.Tensor, ids, rows: torch.Tensor) -> None:
         pool[int(ids[full]), :, :rem, :] = rows[full * bs:].permute(1, 0, 2)
 
 
-def _seq_rows(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
-    """Sequence s's K and V rows from its own stream [seed, 3, s]."""
+def _seq_rows(seed: int, s: int, n: int, hkv: int, d: int, dtype: str, v_mult: float = 1.0):
+    """Sequence s's K and V rows from its own stream [seed, 3, s]; the V
+    draws are multiplied by v_mult before rounding."""
     rng = np.random.default_rng([seed, 3, s])
     k = _round(rng.standard_normal((n, hkv, d), dtype=np.float32), dtype)
-    v = _round(rng.standard_normal((n, hkv, d), dtype=np.float32), dtype)
+    v = _round(rng.standard_normal((n, hkv, d), dtype=np.float32) * np.float32(v_mult), dtype)
     return k, v
 
 
-def _all_rows(seed: int, counts, hkv: int, d: int, dtype: str, fn=None):
+def _all_rows(seed: int, counts, hkv: int, d: int, dtype: str, fn=None, **kw):
     """Rows of every sequence, drawn on a thread pool (numpy releases the GIL)."""
     fn = _seq_rows if fn is None else fn
     workers = max(1, min(16, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
-        futs = [ex.submit(fn, seed, s, int(n), hkv, d, dtype)
+        futs = [ex.submit(fn, seed, s, int(n), hkv, d, dtype, **kw)
                 for s, n in enumerate(counts)]
         return [f.result() for f in futs]
 
@@ -160,18 +162,24 @@ FP8_MAX_MAG_CODE = 0x77
 FP8_DEFAULT_SCALE = 2.0 ** -6
 
 
-def fp8_codes(rng: np.random.Generator, shape) -> torch.Tensor:
+FP8_MAX_FINITE_CODE = 0x7E   # 448, the largest finite E4M3 magnitude
+
+
+def fp8_codes(rng: np.random.Generator, shape, max_code: int = FP8_MAX_MAG_CODE) -> torch.Tensor:
     """Random E4M3 codes: uniform sign, magnitude code uniform in
-    [0, FP8_MAX_MAG_CODE]."""
-    mag = rng.integers(0, FP8_MAX_MAG_CODE + 1, size=shape, dtype=np.uint8)
+    [0, max_code] (at most FP8_MAX_FINITE_CODE: no NaN codes)."""
+    if not 0 <= max_code <= FP8_MAX_FINITE_CODE:
+        raise ValueError(f"max_code must be in [0, 0x7E], got {max_code:#x}")
+    mag = rng.integers(0, max_code + 1, size=shape, dtype=np.uint8)
     sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
     return torch.from_numpy(mag | sign)
 
 
-def _seq_codes(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
+def _seq_codes(seed: int, s: int, n: int, hkv: int, d: int, dtype: str,
+               max_code: int = FP8_MAX_MAG_CODE):
     """Sequence s's K and V codes for n stored positions, stream [seed, 6, s]."""
     rng = np.random.default_rng([seed, 6, s])
-    return fp8_codes(rng, (n, hkv, d)), fp8_codes(rng, (n, hkv, d))
+    return fp8_codes(rng, (n, hkv, d), max_code), fp8_codes(rng, (n, hkv, d), max_code)
 
 
 def _seq_new_rows(seed: int, s: int, n: int, hkv: int, d: int, dtype: str):
@@ -212,7 +220,8 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
                       pool_slack: float = 0.10, scale: Optional[float] = None,
                       pad_tokens: int = 0, placement_seed: Optional[int] = None,
                       kv: str = "16", k_scale: float = FP8_DEFAULT_SCALE,
-                      v_scale: float = FP8_DEFAULT_SCALE) -> PagedBatch:
+                      v_scale: float = FP8_DEFAULT_SCALE, v_mult: float = 1.0,
+                      fp8_max_code: int = FP8_MAX_MAG_CODE) -> PagedBatch:
     """A batch of independent sequences (no sharing).
 
     ``context_lens[s]`` tokens are already in the pool; ``append`` (a count,
@@ -222,7 +231,9 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     new-token rows with slot -1 are interleaved (the append skips them).
     ``placement_seed`` (default ``seed``) changes only where blocks go.
     ``kv="fp8"``: 8-bit pools of E4M3 codes with scales k_scale / v_scale
-    (the 16-bit ``dtype`` is then that of q, the new rows and the output).
+    (the 16-bit ``dtype`` is then that of q, the new rows and the output),
+    magnitude codes drawn up to ``fp8_max_code`` (0x7E: every finite code).
+    ``v_mult`` multiplies the 16-bit V draws (values N(0, v_mult^2)).
     """
     if kv not in ("16", "fp8"):
         raise ValueError(f"kv must be '16' or 'fp8', got {kv!r}")
@@ -257,12 +268,12 @@ def make_decode_batch(name: str, context_lens, num_q_heads: int, num_kv_heads: i
     if kv == "fp8":
         k_pool = torch.full((num_blocks, Hkv, bs, d), FP8_NAN, dtype=torch.uint8)
         v_pool = torch.full((num_blocks, Hkv, bs, d), FP8_NAN, dtype=torch.uint8)
-        codes = _all_rows(seed, ctx, Hkv, d, dtype, _seq_codes)
+        codes = _all_rows(seed, ctx, Hkv, d, dtype, _seq_codes, max_code=fp8_max_code)
         fresh = _all_rows(seed, lens - ctx, Hkv, d, dtype, _seq_new_rows)
     else:
         k_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
         v_pool = _nan_pool(num_blocks, Hkv, bs, d, dtype)
-        rows = _all_rows(seed, lens, Hkv, d, dtype)
+        rows = _all_rows(seed, lens, Hkv, d, dtype, v_mult=v_mult)
     for s in range(S):
         L = int(lens[s])
         c = int(ctx[s])
@@ -374,7 +385,7 @@ def make_long_context(block_size: int, seed: int = 5, num_seqs: int = 32, lo: in
 def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
                        tail_lo: int = 1, tail_hi: int = 512, num_q_heads: int = 32,
                        num_kv_heads: int = 8, head_dim: int = 128, block_size: int = 16,
-                       dtype: str = "f16") -> PagedBatch:
+                       dtype: str = "f16", private_prefix: bool = False) -> PagedBatch:
     """Shared-prefix / beam case.
 
     All sequences reference the same physical blocks holding prefix tokens
@@ -384,6 +395,11 @@ def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
     (copy-on-write) into a private block and appends the sequence's tail from
     offset bs - r_s.  Even-indexed sequences append their tail into fresh
     blocks.  Tails are uniform in [tail_lo, tail_hi] tokens.
+
+    ``private_prefix=True`` builds the same sequences with no sharing: each
+    holds its own copy of the prefix blocks (same rows, its own physical
+    ids), so the step has no copy-on-write pair; the logical K/V of every
+    sequence after the step is the same as with sharing.
     """
     assert prefix % block_size == 0
     bs, d, Hq, Hkv = block_size, head_dim, num_q_heads, num_kv_heads
@@ -395,16 +411,21 @@ def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
     own_prefix = prefix - r
     lens = own_prefix + tails
     n_shared = prefix // bs
-    need = n_shared + int(odd.sum()) + sum(
-        _blocks(int(L), bs) - n_shared for L in lens)
+    if private_prefix:
+        need = sum(max(_blocks(int(L), bs), n_shared) for L in lens)
+    else:
+        need = n_shared + int(odd.sum()) + sum(_blocks(int(L), bs) - n_shared for L in lens)
     num_blocks = int(math.ceil(1.1 * need)) + 1
     rng_place = np.random.default_rng([seed, 1, bs])
     free = _FreeList(num_blocks, rng_place)
-    shared = free.take(n_shared)
+    shared = None if private_prefix else free.take(n_shared)
     owned, pairs = [], []
     for s in range(num_seqs):
-        ids = shared.copy()
-        if r[s] > 0:  # copy-on-write of the shared partial block
+        if private_prefix:
+            ids = free.take(n_shared)
+        else:
+            ids = shared.copy()
+        if r[s] > 0 and not private_prefix:  # copy-on-write of the shared partial block
             dst = int(free.take(1)[0])
             pairs.append((int(shared[-1]), dst))
             ids[-1] = dst
@@ -425,8 +446,13 @@ def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
     rng_pre = np.random.default_rng([seed, 4])
     Kp = _round(rng_pre.standard_normal((prefix, Hkv, d), dtype=np.float32), dtype)
     Vp = _round(rng_pre.standard_normal((prefix, Hkv, d), dtype=np.float32), dtype)
-    _place(k_pool, shared, Kp)
-    _place(v_pool, shared, Vp)
+    if private_prefix:
+        for s in range(num_seqs):
+            _place(k_pool, owned[s][:n_shared], Kp)
+            _place(v_pool, owned[s][:n_shared], Vp)
+    else:
+        _place(k_pool, shared, Kp)
+        _place(v_pool, shared, Vp)
     new_k, new_v, seqs, poss = [], [], [], []
     rows = _all_rows(seed, tails, Hkv, d, dtype)
     for s in range(num_seqs):
@@ -449,8 +475,8 @@ def make_shared_prefix(seed: int = 4, num_seqs: int = 64, prefix: int = 2048,
                       append_seq=np.asarray(seqs, np.int32), append_pos=np.asarray(poss, np.int32),
                       block_mapping=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
                       poison_block=poison,
-                      info={"shared_blocks": shared.copy(), "r": r, "tails": tails,
-                            "prefix": prefix})
+                      info={"shared_blocks": None if shared is None else shared.copy(), "r": r,
+                            "tails": tails, "prefix": prefix})
 
 
 def make_prefill_batch(name: str, context_lens, chunk_lens, num_q_heads: int,

@@ -13,7 +13,12 @@ The five workloads (values N(0, 1), sequences of 3 positions or more) keep
 outputs well below that and are held to the plain bound.  Stress inputs
 whose outputs can be large (many sequences of one or two positions) are held
 to it beyond half a unit in the last place of the output type
-(``round_slack=True``); the mean-abs bound is unchanged.
+(``round_slack=True``); the mean-abs bound is unchanged.  Inputs whose
+values are far from unit scale (V up to a hundred or more) give outputs
+whose rounding to the output type alone exceeds the mean-abs bound: those
+are held to both bounds beyond half an ulp (``excess=True``), i.e. to the
+plain tolerance measured from the correctly rounded result, never to a
+widened one.
 """
 import numpy as np
 import torch
@@ -74,11 +79,11 @@ def half_ulp(ref, dtype):
     return np.ldexp(0.5, (e - bits).astype(np.int64))
 
 
-def compare(out_gpu, ref, pairs=None, label="", round_slack=False, value_scale=1.0):
-    """Assert the attention tolerance; returns (max_abs, mean_abs).
-    ``value_scale`` (>= 1) widens both bounds for values larger than unit
-    scale: the rounding of the softmax weights to the input type errs in
-    proportion to the values they weight."""
+def compare(out_gpu, ref, pairs=None, label="", round_slack=False, excess=False):
+    """Assert the attention tolerance (max-abs 1e-2, mean-abs 1e-3); returns
+    (max_abs, mean_abs).  ``round_slack``: the max-abs bound applies beyond
+    half an ulp of the output type at the reference value; ``excess``: both
+    bounds do."""
     got = out_gpu.detach().double().cpu().numpy()
     if pairs is not None:
         idx = np.asarray(pairs)
@@ -86,12 +91,13 @@ def compare(out_gpu, ref, pairs=None, label="", round_slack=False, value_scale=1
     assert np.isfinite(ref).all(), "oracle produced non-finite values"
     assert np.isfinite(got).all(), f"{label}: GPU output has non-finite values"
     err = np.abs(got - ref)
+    if excess:
+        err = np.maximum(err - half_ulp(ref, out_gpu.dtype), 0.0)
     mean = float(err.mean())
-    if round_slack:
+    if round_slack and not excess:
         err = np.maximum(err - half_ulp(ref, out_gpu.dtype), 0.0)
     mx = float(err.max())
-    assert mx <= MAX_ABS * value_scale and mean <= MEAN_ABS * value_scale, \
-        f"{label}: max-abs {mx:.3g} mean-abs {mean:.3g} (value scale {value_scale:g})"
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{label}: max-abs {mx:.3g} mean-abs {mean:.3g}"
     return mx, mean
 
 

@@ -10,13 +10,14 @@ on 8-bit pools, pa_decode_fp8) against the float64 CPU oracle.
   * decode at the attention tolerance (max-abs 1e-2, mean-abs 1e-3) across
     head sizes, block sizes, query groups, output types and scales; with a
     tile of 32 positions, lengths around multiples of 32 and of the block.
-    The tolerance is the one for values of unit scale, and these cases keep
-    V there (|V| <= 240 * v_scale <= 4, what a per-pool scale of amax / 448
-    gives for such data); k_scale is free, as it only sharpens or flattens
-    the softmax.  One case with V up to 96 is held to the tolerance times
-    96 / 3.75: the softmax weights are rounded to the 16-bit type for the
-    P.V product, which errs in proportion to the values they weight (a CPU
-    emulation of exactly that rounding gives the same error);
+    Most cases keep V near unit scale (|V| <= 240 * v_scale <= 4, what a
+    per-pool scale of amax / 448 gives for such data); k_scale is free, as it
+    only sharpens or flattens the softmax.  Two cases draw every finite code
+    (magnitude codes 0x00..0x7E) for K and V, with V up to 448 * 0.25 = 112:
+    they are held to the same tolerance, measured from the correctly rounded
+    result (outputs that large round by more than the mean-abs bound).  The
+    kernel splits each softmax weight into two 16-bit parts for the P.V
+    product, so its error does not grow with |V|;
     many short sequences, one long sequence cut across many waves, empty
     sequences, contract violations (NaN rows of that sequence only);
   * the 256-sequence mixed step at full size over 8-bit pools, on every
@@ -127,14 +128,19 @@ def test_decode_step_matches_oracle(case):
     compare(out, oracle_out_fp8(b, kp, vp), label=name, round_slack=True)
 
 
-def test_large_value_scale():
-    """V up to 240 * 0.4 = 96: the tolerance scaled by 96 / 3.75."""
-    b = wl.make_decode_batch("large_v", [31, 32, 33, 63, 64, 65, 1000], 8, 4, 128, 32, "bf16",
-                             seed=31, append=1, kv="fp8", k_scale=0.011, v_scale=0.4)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_every_finite_code_and_large_values(dtype):
+    """K and V codes drawn over every finite magnitude (0x00..0x7E, up to 448),
+    V up to 112 after the scale: the plain tolerance, beyond half an ulp of
+    the output (outputs reach tens)."""
+    b = wl.make_decode_batch("full_codes", [1, 2, 3, 31, 32, 33, 63, 64, 65, 1000, 4097], 32, 8,
+                             128, 16, dtype, seed=33, append=1, kv="fp8", k_scale=2 ** -6,
+                             v_scale=0.25, fp8_max_code=wl.FP8_MAX_FINITE_CODE)
+    kp8 = b.k_cache.numpy()
+    assert (kp8 & 0x7F).max() == 0x7F and ((kp8 & 0x7F) == 0x7E).any()  # NaN fill + code 448
     out, dev = gpu_step_fp8(b)
     kp, vp = oracle_pools_fp8(b)
-    compare(out, oracle_out_fp8(b, kp, vp), label="large v_scale", round_slack=True,
-            value_scale=96 / 3.75)
+    compare(out, oracle_out_fp8(b, kp, vp), label=f"every finite code {dtype}", excess=True)
 
 
 def test_many_short_sequences():

@@ -116,6 +116,19 @@ def test_empty_and_single_token_sequences():
     assert torch.equal(out.float().cpu(), v)
 
 
+@pytest.mark.parametrize("impl", ["mfma", "valu"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_large_values(dtype, impl):
+    """V ~ N(0, 64^2): the softmax weights' rounding must not grow with |V|
+    (the matrix-core kernel splits each weight into two 16-bit parts).  The
+    plain tolerance, beyond half an ulp of the output (outputs reach tens)."""
+    b = wl.make_decode_batch("large_v", [1, 2, 3, 15, 16, 17, 100, 1000, 4097], 32, 8, 128, 16,
+                             dtype, seed=9, append=1, v_mult=64.0)
+    out, dev = gpu_step(b, impl=impl)
+    kp, vp = _check_pools(dev, b)
+    compare(out, oracle_out(b, kp, vp), label=f"large values {dtype} {impl}", excess=True)
+
+
 def test_padding_slots_are_skipped():
     b = wl.make_decode_batch("pad", [5, 40, 16], 8, 2, 64, 16, "f16", seed=8, append=1,
                              pad_tokens=5)

@@ -114,3 +114,59 @@ def test_fp8_pools_hold_drawn_codes_and_nan_elsewhere():
     # the appended rows are 16-bit values, one per sequence
     assert b.new_key.dtype == torch.bfloat16 and b.new_key.shape == (4, 2, 64)
     assert b.kv_bytes() == int(b.seq_lens.sum()) * 2 * 2 * 64
+
+
+def _logical_rows(b, kp, vp):
+    """K and V rows of every sequence's positions 0..L-1, read through its table."""
+    rows = []
+    for s, L in enumerate(b.seq_lens):
+        ids = b.block_tables[s]
+        t = np.arange(int(L))
+        rows.append((kp[ids[t // b.block_size], :, t % b.block_size],
+                     vp[ids[t // b.block_size], :, t % b.block_size]))
+    return rows
+
+
+def test_private_prefix_twin_holds_the_same_logical_rows(oracle_mod):
+    """make_shared_prefix(private_prefix=True): no copy-on-write pair, no
+    shared block, and after the step every sequence reads the same rows as
+    with the shared prefix."""
+    kw = dict(num_seqs=10, prefix=96, tail_hi=50)
+    a, b = wl.make_shared_prefix(**kw), wl.make_shared_prefix(private_prefix=True, **kw)
+    assert len(a.block_mapping) == 5 and len(b.block_mapping) == 0
+    assert np.array_equal(a.seq_lens, b.seq_lens)
+    owned = [set(r[:-(-int(L) // 16)]) for r, L in zip(b.block_tables, b.seq_lens)]
+    assert all(not (owned[i] & owned[j]) for i in range(10) for j in range(i))
+    pools = []
+    for x in (a, b):
+        kp, vp = bits(x.k_cache).copy(), bits(x.v_cache).copy()
+        oracle_mod.copy_blocks(kp, vp, x.block_mapping)
+        oracle_mod.reshape_and_cache(bits(x.new_key), bits(x.new_value), kp, vp, x.slot_mapping)
+        pools.append(_logical_rows(x, kp, vp))
+    for (ka, va), (kb, vb) in zip(*pools):
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+
+
+def test_fp8_code_range():
+    lens = [40, 33, 17]
+    a = wl.make_decode_batch("c", lens, 8, 2, 64, 16, "bf16", 3, append=0, kv="fp8")
+    b = wl.make_decode_batch("c", lens, 8, 2, 64, 16, "bf16", 3, append=0, kv="fp8",
+                             fp8_max_code=wl.FP8_MAX_FINITE_CODE)
+    live = lambda x: np.concatenate([r.reshape(-1) for pair in _logical_rows(
+        x, x.k_cache.numpy(), x.v_cache.numpy()) for r in pair])
+    ca, cb = live(a) & 0x7F, live(b) & 0x7F
+    assert ca.max() <= wl.FP8_MAX_MAG_CODE
+    assert cb.max() == wl.FP8_MAX_FINITE_CODE and (cb > wl.FP8_MAX_MAG_CODE).any()
+    with pytest.raises(ValueError):
+        wl.make_decode_batch("c", lens, 8, 2, 64, 16, "bf16", 3, kv="fp8", fp8_max_code=0x7F)
+
+
+def test_v_mult_scales_only_the_values():
+    lens = [20, 7]
+    a = wl.make_decode_batch("m", lens, 8, 2, 64, 16, "bf16", 4)
+    b = wl.make_decode_batch("m", lens, 8, 2, 64, 16, "bf16", 4, v_mult=64.0)
+    assert np.array_equal(bits(a.k_cache), bits(b.k_cache))
+    assert np.array_equal(bits(a.q), bits(b.q))
+    live = ~torch.isnan(a.v_cache)
+    # a power of two commutes with rounding to bf16 (float32's exponent range)
+    assert torch.equal(a.v_cache[live].float() * 64, b.v_cache[live].float())
