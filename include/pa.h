@@ -129,6 +129,34 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments (less the workspace), contract, kernels
+ * and results as pa_decode; the balanced split's partial states live in a
+ * static device array of 24 MiB that the library holds on each GPU it runs
+ * on until the process ends.  That holds every size whose pa_decode
+ * workspace (pa_decode_workspace_bytes, on the current device) fits 24 MiB:
+ * on a 256-CU MI355X, the 16.3 MiB of partial states at head_dim 128 plus
+ * 16 bytes per (sequence, query head), up to about 500,000 of them.  Larger
+ * sizes fail with PA_ERR_WORKSPACE and launch nothing.  The call allocates
+ * nothing: its first call on a device looks up the array's address there
+ * (hipGetSymbolAddress), later calls reuse it.  Nothing in the array needs
+ * to start at zero (every partial a call reads is written by the same call).
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls in one stream are ordered and safe.
+ *
+ * Errors: as pa_decode, PA_ERR_WORKSPACE for sizes beyond the array, and
+ * PA_ERR_HIP if the array's address cannot be found on the current device.
+ */
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t num_blocks, float scale, int32_t partition_size,
+                            pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_decode computed by the wave-level vector kernel instead of the
  * matrix-core one: q.K as packed dot products reduced across the lanes of a
  * row, P.V as float32 FMAs.  Same arguments, contract, workspace and errors

@@ -5,10 +5,10 @@ of ``include/pa.h``); :mod:`.binding` is its Python binding.  Importing this
 package does not load the library; the first use of one of its names does,
 and fails loudly if it has not been built.
 """
-_BINDING_NAMES = ("decode", "reshape_and_cache", "copy_blocks", "decode_workspace_bytes",
-                  "decode_fp8", "reshape_and_cache_fp8", "prefill", "probe_gather", "probe_stream",
-                  "BlockManager",
-                  "NoBlocks", "PaError", "abi_version", "LIB_PATH")
+_BINDING_NAMES = ("decode", "decode_noalloc", "reshape_and_cache", "copy_blocks",
+                  "decode_workspace_bytes", "decode_fp8", "reshape_and_cache_fp8", "prefill",
+                  "probe_gather", "probe_stream", "BlockManager", "NoBlocks", "PaError",
+                  "abi_version", "LIB_PATH")
 
 
 def __getattr__(name):

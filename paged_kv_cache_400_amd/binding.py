@@ -29,6 +29,8 @@ _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c
 SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp]),
     "pa_decode_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -166,6 +168,35 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_si
     _check(fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
               _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB, float(scale),
               int(partition_size), _DT[q.dtype], _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, out, scale=None,
+                   partition_size=0):
+    """pa_decode_noalloc: decode with the library's static scratch instead of a
+    workspace; ``out`` [S][Hq][d] is required (nothing is allocated here
+    either).  Calls that overlap on one GPU race on that scratch."""
+    _need(q, "q", 3)
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    _need(k_cache, "k_cache", 4, q.dtype, dev)
+    _need(v_cache, "v_cache", 4, q.dtype, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    _need(out, "out", 3, q.dtype, dev)
+    if k_cache.shape != v_cache.shape or out.shape != q.shape:
+        raise ValueError("k_cache and v_cache must match, and out must have q's shape")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("inconsistent shapes between q, the pools, block_tables and seq_lens")
+    if scale is None:
+        scale = d ** -0.5
+    _check(_lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs,
+                                  block_tables.shape[1], NB, float(scale), int(partition_size),
+                                  _DT[q.dtype], _stream(dev)))
     return out
 
 

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "pa.h"
 #include "pa_probe.h"
 #include "pa_launch.h"
@@ -123,6 +125,44 @@ enum class Impl { kMfma, kValu };
 
 bool positive_finite(float x) { return x > 0.0f && x <= 3.4028234663852886e38f; }
 
+// ---- the static scratch of pa_decode_noalloc ------------------------------
+// The balanced decode's partial states and pair records, for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy of this
+// array until the process ends.  In host code `scratch` names a host-side
+// stand-in, not a device address: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[pa::kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device).
+pa_status static_scratch(const char* fn, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: no current device: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= pa::kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library serves", fn, dev,
+                pa::kMaxDevices);
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev];
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(PA_ERR_HIP, "%s: the static scratch has no address on device %d: %s", fn,
+                    dev, hipGetErrorString(e));
+      __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
+
 // kv_fp8: 8-bit E4M3 pools with scales k_scale / v_scale (pa_decode_fp8;
 // balanced split only).
 pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
@@ -131,7 +171,8 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                       int32_t num_blocks, float scale, int32_t partition_size, pa_dtype dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f) {
+                      bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f,
+                      bool use_static_scratch = false) {
   g_last_error[0] = '\0';
   if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale)))
     return fail(PA_ERR_SHAPE, "pa_decode_fp8: k_scale %g and v_scale %g must be positive and "
@@ -177,6 +218,17 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
       balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim, waves)
                : partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                                              block_size, partition_size);
+  if (use_static_scratch) {  // pa_decode_noalloc: the scratch replaces the workspace
+    if (need > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "pa_decode_noalloc: these sizes need %zu bytes of scratch (the partial states "
+                  "of %d waves at head_dim %d, plus 16 bytes per (sequence, query head)); the "
+                  "library's static scratch holds %zu",
+                  need, waves, head_dim, kScratchBytes);
+    const pa_status st = static_scratch("pa_decode_noalloc", &workspace);
+    if (st != PA_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
@@ -252,6 +304,18 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, scale, partition_size, dtype, workspace, workspace_bytes,
                      stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t num_blocks, float scale, int32_t partition_size,
+                            pa_dtype dtype, hipStream_t stream) {
+  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, scale, partition_size, dtype, nullptr, 0, stream, false, 1.0f,
+                     1.0f, true);
 }
 
 pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,

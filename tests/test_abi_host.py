@@ -157,3 +157,17 @@ def test_probe_stream_rejects_bad_arguments(lib):
     assert lib.pa_probe_stream(P, P + 8, 1 << 20, NULL) == 2      # misaligned
     assert "aligned" in lib.pa_last_error().decode()
     assert lib.pa_probe_stream(P, P, 1000, NULL) == 2             # not a multiple of 16
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """pa_decode_noalloc refuses sizes whose partial states and records do
+    not fit the library's 24 MiB static scratch, before touching the device."""
+    P = 1 << 12
+    S = 600_000  # 600k x 8 query heads of 16-byte records alone exceed 24 MiB
+    st = lib.pa_decode_noalloc(P, P, P, P, P, P, S, 8, 2, 128, 16, 1, 64, 0.125, 0, 1, NULL)
+    assert st == 4
+    assert "static scratch" in lib.pa_last_error().decode()
+    # argument errors come first, as for pa_decode
+    assert lib.pa_decode_noalloc(P, NULL, P, P, P, P, 2, 8, 2, 128, 16, 4, 64, 0.125, 0, 1,
+                                 NULL) == 1
+
