@@ -86,11 +86,16 @@ KERNEL_SOURCES = {
 }
 KERNEL_NAMES = {
     ("fp8", True): "pa_decode_fp8 (pa_decode_streamk over E4M3 pools + pa_streamk_reduce)",
-    ("mfma", True): "pa_decode (pa_decode_streamk + pa_streamk_reduce)",
-    ("mfma", False): ("pa_decode, explicit partitions (pa_decode_streamk with runs cut at "
+    ("auto", True): "pa_decode (pa_decode_streamk + pa_streamk_reduce)",
+    ("auto", False): ("pa_decode, explicit partitions (pa_decode_streamk with runs cut at "
                       "partition boundaries + pa_streamk_reduce)"),
-    ("valu", True): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
-    ("valu", False): "pa_decode_valu (pa_decode_valu + pa_splitk_reduce)",
+    ("mfma", True): ("pa_probe_decode_mfma (pa_decode_streamk with the matrix-core tile wave "
+                     "at every group + pa_streamk_reduce)"),
+    ("mfma", False): ("pa_probe_decode_mfma, explicit partitions (pa_decode_streamk with the "
+                      "matrix-core tile wave + pa_streamk_reduce)"),
+    ("valu", True): ("pa_decode_valu, balanced split (pa_decode_streamk with the vector-unit "
+                     "tile wave + pa_streamk_reduce)"),
+    ("valu", False): "pa_decode_valu, fixed partitions (pa_decode_valu + pa_splitk_reduce)",
 }
 
 
@@ -149,7 +154,8 @@ def parse():
     ap.add_argument("--kv", choices=["16", "fp8"], default="16",
                     help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
                          "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
-    ap.add_argument("--mode", choices=["decode", "prefill", "serve", "long"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "serve", "long", "groups"],
+                    default="decode",
                     help="decode: the mixed decode step (the headline); prefill: the chunked "
                          "prefill step (32 sequences x 512-token chunks, pa_prefill); serve: "
                          "iteration-level batching over the paged pool against 4096-token "
@@ -169,8 +175,10 @@ def parse():
                          "summary object")
     ap.add_argument("--fp8-summary", choices=["on", "off"], default="on",
                     help="with --kv 16: also time the 8-bit step and add a summary object")
-    ap.add_argument("--impl", choices=["mfma", "valu"], default="mfma",
-                    help="pa_decode (matrix-core kernel) or pa_decode_valu")
+    ap.add_argument("--impl", choices=["auto", "mfma", "valu"], default="auto",
+                    help="auto: pa_decode (tile wave chosen by the query group); mfma: "
+                         "pa_probe_decode_mfma (matrix cores at every group); valu: "
+                         "pa_decode_valu (vector unit alone)")
     ap.add_argument("--block-manager", choices=["on", "off"], default="on",
                     help="time the host block manager's bookkeeping for the same step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -540,13 +548,14 @@ def long_context_summary(args, block_sizes=(8, 16, 32)):
         out = torch.empty_like(dev["q"])
         row = {"kv_bytes": kv, "num_blocks": b.num_blocks,
                "max_blocks_per_seq": b.max_blocks_per_seq}
-        for name, part in (("balanced", 0), ("partitions_512", 512)):
+        for name, part, impl in (("balanced", 0, "auto"), ("partitions_512", 512, "auto"),
+                                 ("valu_balanced", 0, "valu")):
             need = pa.decode_workspace_bytes(S, Hq, d, b.max_blocks_per_seq, bs, part)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
             ms = time_calls(lambda: pa.decode(dev["q"], dev["k_cache"], dev["v_cache"],
                                               dev["block_tables"], dev["seq_lens"],
                                               scale=b.scale, partition_size=part, out=out,
-                                              workspace=ws), steps, args.warmup)
+                                              workspace=ws, impl=impl), steps, args.warmup)
             gbs = kv / (ms * 1e-3) / 1e9
             row[name] = {"decode_ms": round(ms, 5), "gbs": round(gbs, 2),
                          "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -676,6 +685,72 @@ def serve_line(args):
     }
 
 
+GROUPS_WORKLOAD = ("group sweep: the mixed step's 256 sequences (context uniform[64,4096] + 1), "
+                   "8 kv heads, d 128, bf16, block 16, with 8, 16, 32 and 64 query heads "
+                   "(group 1, 2, 4, 8): the same K/V bytes, 1 to 8 query heads per byte; "
+                   "decode only")
+
+
+def group_sweep(args, groups=(1, 2, 4, 8)):
+    """The balanced split with the matrix-core tile wave (pa_probe_decode_mfma)
+    against the same split with the vector-unit tile wave (pa_decode_valu,
+    partition_size 0: the same runs, launch and merge), and pa_decode (which
+    picks one of the two by the group), on the mixed step's K/V at each query
+    group: mean us per call over back-to-back calls (HIP events), effective
+    KV GB/s, and the vector kernel's time over the matrix-core one's.  One
+    batch is drawn with 64 query heads; group g decodes its first 8 g heads."""
+    import torch
+    import paged_kv_cache_400_amd as pa
+    from paged_kv_cache_400_amd import workload as wl
+    ctx = wl.mixed_lengths(256, 64, 4096, 3)
+    b = wl.make_decode_batch("group_sweep", ctx, 64, 8, 128, 16, "bf16", 3, append=1)
+    dev = wl.to_device(b, "cuda:0")
+    pa.reshape_and_cache(dev["new_key"], dev["new_value"], dev["k_cache"], dev["v_cache"],
+                         dev["slot_mapping"])
+    kv = b.kv_bytes()
+    steps = max(1, min(args.steps, 50))
+    res = {"workload": GROUPS_WORKLOAD + " (bench.py --mode groups)", "kv_bytes": kv}
+    for g in groups:
+        q = dev["q"][:, :8 * g].contiguous()
+        S, Hq, d = q.shape
+        need = pa.decode_workspace_bytes(S, Hq, d, b.max_blocks_per_seq, 16, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
+        out = torch.empty_like(q)
+        row = {}
+        for impl in ("mfma", "valu", "auto"):
+            ms = time_calls(lambda: pa.decode(q, dev["k_cache"], dev["v_cache"],
+                                              dev["block_tables"], dev["seq_lens"],
+                                              scale=b.scale, out=out, workspace=ws, impl=impl),
+                            steps, args.warmup)
+            gbs = kv / (ms * 1e-3) / 1e9
+            row[impl] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 2),
+                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        row["valu_over_mfma_time"] = round(row["valu"]["us"] / row["mfma"]["us"], 4)
+        res[f"g{g}"] = row
+        del ws
+    return res
+
+
+def groups_line(args):
+    """The group sweep as the line's workload: value = pa_decode's effective
+    KV GB/s at group 4 (the mixed step itself); every group and both tile
+    waves in `group_sweep`."""
+    gs = group_sweep(args)
+    row = gs["g4"]["auto"]
+    return {
+        "metric": METRIC, "value": row["gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": max(1, min(args.steps, 50)), "warmup": args.warmup,
+        "ms_per_step": round(row["us"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": GROUPS_WORKLOAD, "kv_bytes": gs["kv_bytes"]},
+        "roofline": {"kernel": KERNEL_NAMES[("auto", True)], "bound": "hbm",
+                     "achieved": row["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": row["frac_of_hbm_peak"], "traffic": None,
+                     "traffic_source": "not profiled"},
+        "group_sweep": gs,
+    }
+
+
 def long_line(args):
     """The long-context batch as the line's workload: value = effective KV
     GB/s of pa_decode (balanced split) at block size 16; every block size
@@ -691,7 +766,7 @@ def long_line(args):
                    "kv_bytes": lc["bs16"]["kv_bytes"]},
         "frac_of_hbm_peak": row["frac_of_hbm_peak"],
         "decode_seqs_per_s": row["decode_seqs_per_s"],
-        "roofline": {"kernel": KERNEL_NAMES[("mfma", True)], "bound": "hbm",
+        "roofline": {"kernel": KERNEL_NAMES[("auto", True)], "bound": "hbm",
                      "achieved": row["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": row["frac_of_hbm_peak"], "traffic": None,
                      "traffic_source": "not profiled"},
@@ -717,6 +792,9 @@ def main():
     if args.mode == "serve":
         print(json.dumps(serve_line(args)), flush=True)
         return
+    if args.mode == "groups":
+        print(json.dumps(groups_line(args)), flush=True)
+        return
     if args.mode == "long":
         print(json.dumps(long_line(args)), flush=True)
         return
@@ -725,7 +803,7 @@ def main():
     dev = wl.to_device(b, "cuda:0")
     S, Hq, d = b.q.shape
     MB, bs = b.max_blocks_per_seq, b.block_size
-    if args.kv == "fp8" and (args.partition_size != 0 or args.impl != "mfma"):
+    if args.kv == "fp8" and (args.partition_size != 0 or args.impl != "auto"):
         print("--kv fp8 runs pa_decode_fp8 (balanced split only)", file=sys.stderr)
         sys.exit(2)
     ms_step, ms_decode, ceiling = measure(b, dev, args, args.kv, args.partition_size,
@@ -795,7 +873,7 @@ def main():
             "frac_of_peak": round(gbs_sr / HBM_PEAK_GBS, 4),
             "decode_frac_of_streaming_read": round(gbs_decode / gbs_sr, 4),
         }
-    profiled = args.impl == "mfma" and args.partition_size == 0
+    profiled = args.impl == "auto" and args.partition_size == 0
     traffic, note = measured_traffic(args.kv)
     if profiled and traffic is not None:
         res["roofline"]["traffic"] = traffic

@@ -111,7 +111,13 @@ typedef enum pa_dtype {
  * positions ([k*P, (k+1)*P)), and runs start and end only at partition
  * boundaries: every partial state covers whole partitions, and the
  * partitions one wave walks in a sequence are merged in its registers.
- * Both give the same result up to float32 summation order.  The workspace needs
+ * Both give the same result up to float32 summation order.  The tile wave
+ * (how a run's tiles are computed) is chosen by the query group: at group 1
+ * the vector unit alone (as pa_decode_valu), from group 2 on the matrix
+ * cores (q.K^T and P.V as MFMA, the G query heads on the MFMA's N axis).
+ * Measured on the 256-sequence mixed step at groups 1/2/4/8, the matrix
+ * cores take the same time at group 1 and save 1%, 7% and 46% above it.
+ * The workspace needs
  * pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents on
  * entry do not matter and on return are unspecified.
  *
@@ -157,15 +163,21 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                             pa_dtype dtype, hipStream_t stream);
 
 /*
- * pa_decode computed by the wave-level vector kernel instead of the
- * matrix-core one: q.K as packed dot products reduced across the lanes of a
- * row, P.V as float32 FMAs.  Same arguments, contract, workspace and errors
- * as pa_decode, except that partition_size = 0 means fixed 512-position
- * partitions; results agree to rounding (the two sum in different orders,
- * and this kernel keeps P in float32).  Unlike pa_decode, its result for a
- * sequence does not depend on the other sequences of the batch, bit for
- * bit: every (sequence, KV head, partition) is one workgroup's fixed-order
- * computation, merged in partition order.
+ * pa_decode computed on the vector unit alone instead of the matrix cores:
+ * q.K as packed dot products reduced across the lanes of a row (DPP), the
+ * online softmax per lane, P.V as float32 FMAs with the weights kept in
+ * float32.  Same arguments, contract, workspace and errors as pa_decode;
+ * results agree to rounding (the two sum in different orders).  Work split:
+ * partition_size = 0 is pa_decode's balanced split, the same runs, launch
+ * and merge with the vector tile wave in place of the matrix-core one;
+ * partition_size > 0 (a multiple of 16 and of block_size, at most 512
+ * blocks) gives every (sequence, KV head, partition of that many positions)
+ * its own workgroup, whose four waves take the partition's tiles in turn
+ * and merge through LDS, and a second kernel merges the partitions in
+ * order.  With partition_size > 0 a sequence's result does not depend on
+ * the other sequences of the batch, bit for bit; the balanced split's does
+ * (where its runs cut the sequence depends on the whole batch), within
+ * float32 rounding.
  */
 pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -181,11 +193,11 @@ pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const vo
  * waves per CU of the current device: 2048 waves on a 256-CU MI355X; at
  * most 8192, and 8192 when no device can be queried), min(num_q_heads, 8)
  * heads of head_dim floats plus (m, l) each, and one 16-byte record per
- * (sequence, query head), which pa_decode uses; and the (m, l, acc) per
- * (sequence, query head, partition) of pa_decode_valu's fixed partitions (of
- * partition_size positions, 512 when it is 0), an upper bound from
- * max_blocks_per_seq * block_size that is 0 when no sequence can need more
- * than one partition.  0 when an argument is invalid (pa_decode then
+ * (sequence, query head), which pa_decode (and pa_decode_valu with
+ * partition_size 0) uses; and, for partition_size > 0, the (m, l, acc) per
+ * (sequence, query head, partition) of pa_decode_valu's fixed partitions, an
+ * upper bound from max_blocks_per_seq * block_size that is 0 when no
+ * sequence can need more than one partition.  0 when an argument is invalid (pa_decode then
  * reports the error).  A workspace sized on one device serves calls on any
  * device with as many CUs or fewer.
  */

@@ -38,6 +38,22 @@ pa_status pa_probe_gather(void* sink, const void* k_cache, const void* v_cache,
                           int32_t num_blocks, pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_decode with the matrix-core tile wave at every query group.  pa_decode
+ * chooses the tile wave by the group (the vector unit at group 1, where the
+ * matrix cores save nothing; the matrix cores from group 2, where they do);
+ * this entry point keeps the choice measurable at group 1, and is otherwise
+ * pa_decode: same arguments, contract, workspace, results (to float32
+ * rounding) and errors.
+ */
+pa_status pa_probe_decode_mfma(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                               int32_t partition_size, pa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Reads `bytes` bytes of `buf` once, as a streaming read: every wave reads
  * 1 KiB segments (64 lanes x 16 bytes, the streaming hint), segment w, then
  * w + W, w + 2W, ... for wave w of W, eight in flight, so that the waves

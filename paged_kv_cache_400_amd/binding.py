@@ -31,6 +31,9 @@ SIGNATURES = {
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp]),
+    "pa_probe_decode_mfma": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
+                                            _vp, _sz, _vp]),
     "pa_decode_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -124,17 +127,21 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, 
                                               max_blocks_per_seq, block_size, partition_size))
 
 
+_DECODE_FN = {"auto": "pa_decode", "valu": "pa_decode_valu", "mfma": "pa_probe_decode_mfma"}
+
+
 def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_size=0, out=None,
-           workspace=None, impl="mfma"):
+           workspace=None, impl="auto"):
     """out[s][h] = softmax(scale * q[s][h] . K) V over the sequence's paged K/V.
 
     q [S][Hq][d]; k_cache/v_cache [NB][Hkv][bs][d]; block_tables int32
     [S][MB]; seq_lens int32 [S].  ``workspace`` (a uint8 tensor) is allocated
-    when needed and not given.  ``impl``: "mfma" (pa_decode) or "valu"
-    (pa_decode_valu).
+    when needed and not given.  ``impl``: "auto" (pa_decode, the tile wave
+    chosen by the query group), "valu" (pa_decode_valu, the vector unit
+    alone) or "mfma" (pa_probe_decode_mfma, the matrix cores at every group).
     """
-    if impl not in ("mfma", "valu"):
-        raise ValueError(f"impl must be 'mfma' or 'valu', got {impl!r}")
+    if impl not in _DECODE_FN:
+        raise ValueError(f"impl must be one of {sorted(_DECODE_FN)}, got {impl!r}")
     _need(q, "q", 3)
     dev = q.device
     if q.dtype not in _DT:
@@ -164,7 +171,7 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale=None, partition_si
     if workspace is not None:
         _need(workspace, "workspace", None, None, dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-    fn = _lib.pa_decode if impl == "mfma" else _lib.pa_decode_valu
+    fn = getattr(_lib, _DECODE_FN[impl])
     _check(fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
               _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs, MB, NB, float(scale),
               int(partition_size), _DT[q.dtype], _ptr(workspace), ws_bytes, _stream(dev)))

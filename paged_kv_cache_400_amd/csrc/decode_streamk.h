@@ -53,6 +53,7 @@
 #include "pa_launch.h"
 #include "pa_mfma.h"
 #include "pa_mfma_fp8.h"
+#include "pa_valu.h"
 
 namespace pa {
 
@@ -96,7 +97,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 }  // namespace
 
 // The tile wave of a pool element type: TileWave (pa_mfma.h) for 16-bit
-// pools, TileWave8 (pa_mfma_fp8.h) for 8-bit E4M3 pools.
+// pools, TileWave8 (pa_mfma_fp8.h) for 8-bit E4M3 pools, TileWaveV
+// (pa_valu.h, the vector unit alone) for 16-bit pools tagged Vec.
 template <typename T, typename KV, int D, int BS, int G>
 struct TileWaveOf {
   using type = TileWave<T, D, BS, G>;
@@ -104,6 +106,10 @@ struct TileWaveOf {
 template <typename T, int D, int BS, int G>
 struct TileWaveOf<T, FP8, D, BS, G> {
   using type = TileWave8<T, D, BS, G>;
+};
+template <typename T, int D, int BS, int G>
+struct TileWaveOf<T, Vec, D, BS, G> {
+  using type = TileWaveV<T, D, BS, G>;
 };
 
 // kGather = true is the gather-only instantiation behind pa_probe_gather:
@@ -127,8 +133,8 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   int32_t mb, int32_t nb, int32_t nwaves, int32_t part_tiles, float qk_scale,
                   float out_scale) {
   using TW = typename TileWaveOf<T, KV, D, BS, G>::type;
-  constexpr int KL = TW::KL, NM = TW::NM, kT = TW::kTileLen, kIds = TW::kIds;
-  constexpr bool kScaled = !std::is_same<KV, T>::value;
+  constexpr int KL = TW::KL, kT = TW::kTileLen, kIds = TW::kIds;
+  constexpr bool kScaled = std::is_same<KV, FP8>::value;
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * TW::kTileBytes];
   static_assert(sizeof(s_mem) <= kMaxLdsBytes, "one workgroup's LDS fits gfx950's 160 KiB");
   static_assert(kWorkgroupsPerCu * sizeof(s_mem) <= kMaxLdsBytes,
@@ -237,24 +243,12 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   // staged row-major in the wave's V tiles (idle once the last tile is
   // consumed) and stored 16 bytes per lane: whole, contiguous cache lines.
   // (Stores of 32 or 64 bytes per instruction cost the mixed decode step 2%.)
+  unsigned char* vtile = s_mem + w * 2 * TW::kTileBytes;
   auto write_result = [&](const TW& t, bool bad, int64_t row0, int t_lo,
                           int t_hi, int ns, bool first, int64_t pair_ustart) {
-    const int col = lane & 15, grp = lane >> 4;
     const bool whole = t_lo == 0 && t_hi == ns;
-    float* st = reinterpret_cast<float*>(t.vtile);  // [G][D]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * grp + r;
-      const float l_h = __shfl(t.l_run, h);
-      if (h < G) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          float v = whole ? t.acc[m][r] / l_h : t.acc[m][r];
-          if constexpr (kScaled) v *= out_scale;
-          st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : v;
-        }
-      }
-    }
+    float* st = reinterpret_cast<float*>(vtile);  // [G][D]
+    t.stage(st, whole, bad, kScaled ? out_scale : 1.0f);
     // one wave's LDS accesses take effect in program order
     if (whole) {
       for (int i = lane * 8; i < G * D; i += 64 * 8) {
@@ -269,8 +263,8 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       for (int i = lane * 4; i < G * D; i += 64 * 4)
         *reinterpret_cast<float4*>(ws_acc + slot * G * D + i) =
             *reinterpret_cast<const float4*>(st + i);
-      if (lane < G)
-        ws_ml[slot * G + lane] = make_float2(t.m_run, bad ? __builtin_nanf("") : t.l_run);
+      const float2 ml = t.ml_of_lane();
+      if (lane < G) ws_ml[slot * G + lane] = make_float2(ml.x, bad ? __builtin_nanf("") : ml.y);
     }
     if (t_hi == ns && lane == 0) {
       const int c_first = (int)(pair_ustart / chunk);
@@ -281,7 +275,6 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   static_assert(sizeof(float) * G * D <= 2 * TW::kTileBytes, "the result fits the wave's V tiles");
 
   TW tw;
-  unsigned char* vtile = s_mem + w * 2 * TW::kTileBytes;
 
   int64_t g = g0;
   while (true) {
@@ -489,17 +482,21 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   const int cap = gather ? kStreamKMaxWaves : min(a.max_waves, kStreamKMaxWaves);
   if (a.num_kv_heads > cap) return hipErrorInvalidValue;
   waves = max(min(waves, cap) / a.num_kv_heads, 1) * a.num_kv_heads;
-  if (gather) {  // the same grid, gather-only (the group does not change the loads)
-    static int lds_cache[kMaxDevices];
-    auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV>;
-    e = check_lds((const void*)kernel, 0, lds_cache);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
-                       dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr, nullptr,
-                       nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
-                       a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
-                       a.max_blocks_per_seq, a.num_blocks, waves, 0, 0.0f, 0.0f);
-    return hipGetLastError();
+  if constexpr (!std::is_same<KV, Vec>::value) {  // the gather probe reads as the matrix-core wave
+    if (gather) {  // the same grid, gather-only (the group does not change the loads)
+      static int lds_cache[kMaxDevices];
+      auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV>;
+      e = check_lds((const void*)kernel, 0, lds_cache);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kernel, dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
+                         dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr,
+                         nullptr, nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
+                         a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
+                         a.max_blocks_per_seq, a.num_blocks, waves, 0, 0.0f, 0.0f);
+      return hipGetLastError();
+    }
+  } else {
+    if (gather) return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>),
                      dim3((uint32_t)((waves + kWaves - 1) / kWaves)),

@@ -1,12 +1,17 @@
 // decode_streamk.hip -- the balanced (stream-K) decode of decode_streamk.h
-// instantiated for 16-bit pools (pa_decode's automatic mode and
-// pa_probe_gather).
+// instantiated for 16-bit pools: with the matrix-core tile wave (pa_decode,
+// pa_probe_gather) and with the vector-unit one (pa_decode_valu's balanced
+// mode).
 #include "decode_streamk.h"
 
 namespace pa {
 
 hipError_t launch_decode_streamk(const StreamKArgs& a) {
   return a.bf16 ? launch_d<BF16, BF16>(a, false) : launch_d<F16, F16>(a, false);
+}
+
+hipError_t launch_decode_streamk_valu(const StreamKArgs& a) {
+  return a.bf16 ? launch_d<BF16, Vec>(a, false) : launch_d<F16, Vec>(a, false);
 }
 
 hipError_t launch_gather_streamk(const StreamKArgs& a) {

@@ -106,12 +106,15 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
       resolve_partition(partition_size, block_size) == 0)
     return 0;
-  const size_t part_bytes = partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                        max_blocks_per_seq, block_size,
-                                                        partition_size);
-  // pa_decode runs the balanced kernel (partition-aligned runs when
-  // partition_size > 0), pa_decode_valu fixed partitions (512 positions when
-  // partition_size is 0); the workspace serves either
+  // pa_decode runs the balanced split (partition-aligned runs when
+  // partition_size > 0), and so does pa_decode_valu when partition_size is
+  // 0; pa_decode_valu with partition_size > 0 runs fixed partitions.  The
+  // workspace serves either entry point.
+  const size_t part_bytes =
+      partition_size > 0 ? partitioned_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                       max_blocks_per_seq, block_size,
+                                                       partition_size)
+                         : 0;
   const size_t sk = (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim,
                                                         pa::streamk_device_waves());
   return sk > part_bytes ? sk : part_bytes;
@@ -121,7 +124,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 namespace {
 
-enum class Impl { kMfma, kValu };
+// kAuto: pa_decode, the balanced split with the tile wave chosen by the
+// query group (the vector unit at group 1, the matrix cores above; measured
+// on the mixed step: at group 1 the two take the same time, the matrix cores
+// save 1%, 7% and 46% at groups 2, 4 and 8).  kMfma: the matrix-core tile
+// wave at every group (pa_probe_decode_mfma).  kValu: pa_decode_valu.
+enum class Impl { kAuto, kMfma, kValu };
 
 bool positive_finite(float x) { return x > 0.0f && x <= 3.4028234663852886e38f; }
 
@@ -212,7 +220,8 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
   if (units * 256 >= kMaxThreadsPerLaunch || pmax > INT32_MAX)
     return fail(PA_ERR_SHAPE, "pa_decode: %lld work units exceed one launch",
                 (long long)units);
-  const bool balanced = impl == Impl::kMfma;
+  // the balanced split: pa_decode always, pa_decode_valu with partition_size 0
+  const bool balanced = impl != Impl::kValu || partition_size == 0;
   const int waves = pa::streamk_device_waves();
   const size_t need =
       balanced ? (size_t)pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim, waves)
@@ -261,8 +270,12 @@ pa_status decode_impl(Impl impl, void* out, const void* q, const void* k_cache,
     a.out_scale = v_scale;
     a.bf16 = dtype == PA_BF16;
     a.stream = stream;
-    return launch_status(kv_fp8 ? "pa_decode_fp8" : "pa_decode",
-                         kv_fp8 ? pa::launch_decode_streamk_fp8(a) : pa::launch_decode_streamk(a));
+    if (kv_fp8) return launch_status("pa_decode_fp8", pa::launch_decode_streamk_fp8(a));
+    if (impl == Impl::kValu || (impl == Impl::kAuto && group == 1))
+      return launch_status(impl == Impl::kValu ? "pa_decode_valu" : "pa_decode",
+                           pa::launch_decode_streamk_valu(a));
+    return launch_status(impl == Impl::kMfma ? "pa_probe_decode_mfma" : "pa_decode",
+                         pa::launch_decode_streamk(a));
   }
 
   pa::DecodeArgs a;
@@ -300,7 +313,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                     float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+  return decode_impl(Impl::kAuto, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, scale, partition_size, dtype, workspace, workspace_bytes,
                      stream);
@@ -312,7 +325,7 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                             int32_t num_blocks, float scale, int32_t partition_size,
                             pa_dtype dtype, hipStream_t stream) {
-  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+  return decode_impl(Impl::kAuto, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, scale, partition_size, dtype, nullptr, 0, stream, false, 1.0f,
                      1.0f, true);
@@ -336,7 +349,7 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                         float scale, float k_scale, float v_scale, pa_dtype dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+  return decode_impl(Impl::kAuto, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, scale, 0, dtype, workspace, workspace_bytes, stream, true,
                      k_scale, v_scale);
@@ -497,6 +510,19 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
                        pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
                                               num_kv_heads, head_dim, block_size, num_blocks,
                                               dtype == PA_FP8_E4M3 ? 1 : 2, stream));
+}
+
+pa_status pa_probe_decode_mfma(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, float scale,
+                               int32_t partition_size, pa_dtype dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(Impl::kMfma, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, scale, partition_size, dtype, workspace, workspace_bytes,
+                     stream);
 }
 
 pa_status pa_probe_stream(void* sink, const void* buf, size_t bytes, hipStream_t stream) {

@@ -114,6 +114,8 @@ inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 hipError_t launch_decode_streamk(const StreamKArgs& a);
+// The same split with the vector-unit tile wave (pa_valu.h), 16-bit pools.
+hipError_t launch_decode_streamk_valu(const StreamKArgs& a);
 // Gather-only run of the same split and loads (pa_probe_gather); uses only
 // out (a sink word), the pools, block_tables, seq_lens and the sizes.
 hipError_t launch_gather_streamk(const StreamKArgs& a);

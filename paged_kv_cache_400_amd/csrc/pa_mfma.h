@@ -94,6 +94,31 @@ __device__ __forceinline__ void wait_vmem_all() {
   asm volatile("" ::: "memory");
 }
 
+// The G x D result of a matrix-core tile wave, row-major into st: lane (col,
+// grp) holds acc[m][r] for head 4 grp + r, column 16 m + col, and head col's
+// whole denominator in l_run (after finish).  whole: divide by the
+// denominator (a finished row), else the raw accumulator (a partial state);
+// every value times `scale`; NaN everywhere if bad.
+template <int G, int D, int NM>
+__device__ __forceinline__ void stage_mfma_result(float* st, const f32x4_t (&acc)[NM],
+                                                  float l_run, bool whole, bool bad,
+                                                  float scale) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * grp + r;
+    const float l_h = __shfl(l_run, h);
+    if (h < G) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const float v = (whole ? acc[m][r] / l_h : acc[m][r]) * scale;
+        st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : v;
+      }
+    }
+  }
+}
+
 template <int D>
 struct Geo {
   static constexpr int KC = D / 32;                 // q.K^T MFMA steps
@@ -259,6 +284,13 @@ struct TileWave {
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
   }
+
+  // After finish: the result row-major into st ([G][D] floats), and (m, l)
+  // of head `lane` for lanes < G.
+  __device__ __forceinline__ void stage(float* st, bool whole, bool bad, float scale) const {
+    stage_mfma_result<G, D, NM>(st, acc, l_run, whole, bad, scale);
+  }
+  __device__ __forceinline__ float2 ml_of_lane() const { return make_float2(m_run, l_run); }
 };
 
 }  // namespace pa

@@ -247,6 +247,11 @@ struct TileWave8 {
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
   }
+
+  __device__ __forceinline__ void stage(float* st, bool whole, bool bad, float scale) const {
+    stage_mfma_result<G, D, NM>(st, acc, l_run, whole, bad, scale);
+  }
+  __device__ __forceinline__ float2 ml_of_lane() const { return make_float2(m_run, l_run); }
 };
 
 }  // namespace pa

@@ -32,7 +32,7 @@ MEAN_ABS = 1e-3
 ODT = {"f16": oracle.F16, "bf16": oracle.BF16}
 
 
-def gpu_step(b, partition_size=0, device="cuda:0", dev=None, impl="mfma"):
+def gpu_step(b, partition_size=0, device="cuda:0", dev=None, impl="auto"):
     """copy_blocks -> reshape_and_cache -> decode on the GPU; returns (out, dev)."""
     dev = to_device(b, device) if dev is None else dev
     if len(b.block_mapping):

@@ -92,10 +92,10 @@ def test_workspace_bytes(lib):
     assert f(2, 4, 64, 10, 8, 12) == 0          # not a multiple of the block size
     assert f(2, 4, 64, 10, 8, 8 * 513) == 0     # more blocks than a partition holds
 
-    # automatic: pa_decode_valu uses 512-position partitions
+    # automatic: both entry points run the balanced split
     assert f(4, 8, 64, 4, 16, 0) == balanced(4, 8, 64)
-    assert f(256, 32, 128, 257, 16, 0) == max(balanced(256, 32, 128), 256 * 32 * 9 * 130 * 4)
-    assert f(8, 2, 128, 4096, 8, 0) == max(balanced(8, 2, 128), 8 * 2 * 64 * 130 * 4)
+    assert f(256, 32, 128, 257, 16, 0) == balanced(256, 32, 128)
+    assert f(8, 2, 128, 4096, 8, 0) == balanced(8, 2, 128)
 
 
 NULL = None

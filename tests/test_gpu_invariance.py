@@ -9,7 +9,8 @@ and copy-on-write), and the batch a sequence decodes in changes every step
 
   * placement: the same logical K/V under two seeded block placements give
     bit-identical outputs (every entry point: pa_decode automatic and with
-    512-position partitions, pa_decode_valu, pa_decode_fp8).  The kernels
+    512-position partitions, pa_decode_valu balanced and with fixed
+    partitions, pa_decode_fp8).  The kernels
     cut the work by logical position only, so the physical ids cannot change
     a single operation;
   * sharing: the shared-prefix step (one physical copy of the prefix,
@@ -17,14 +18,15 @@ and copy-on-write), and the batch a sequence decodes in changes every step
     same sequences each holding a private copy of the prefix;
   * batch composition: a sequence decoded alone, or inside a smaller batch,
     against the same sequence inside the 256-sequence mixed step.
-    pa_decode_valu is bitwise batch-invariant: every (sequence, head,
-    512-position partition) is computed by one workgroup in a fixed order
-    and the partitions are merged in a fixed order.  pa_decode is not: its
-    balanced split cuts each KV head's tiles into equal runs over the whole
-    batch, so where a sequence's tiles are cut, and so its float32 summation
-    order, depends on its batch-mates.  Its outputs are held to the
-    attention tolerance against each other and against the oracle, and the
-    largest difference is printed.
+    pa_decode_valu with a partition_size (here 512) is bitwise
+    batch-invariant: every (sequence, head, partition) is computed by one
+    workgroup in a fixed order and the partitions are merged in a fixed
+    order.  The balanced split (pa_decode, and pa_decode_valu with
+    partition_size 0) is not: it cuts each KV head's tiles into equal runs
+    over the whole batch, so where a sequence's tiles are cut, and so its
+    float32 summation order, depends on its batch-mates.  Its outputs are
+    held to the attention tolerance against each other and against the
+    oracle, and the largest difference is printed.
 """
 import numpy as np
 import pytest
@@ -62,7 +64,7 @@ def test_block_placement_is_bit_invariant(case):
         if place == 12:
             assert not np.array_equal(b.block_tables, tables), "placements must differ"
         tables = b.block_tables
-        for impl, part in (("mfma", 0), ("mfma", 512), ("valu", 0)):
+        for impl, part in (("auto", 0), ("auto", 512), ("mfma", 0), ("valu", 0), ("valu", 512)):
             fresh = {k: v.clone() for k, v in dev.items()}
             out, _ = gpu_step(b, partition_size=part, dev=fresh, impl=impl)
             outs.setdefault((impl, part), []).append(out.cpu())
@@ -93,28 +95,28 @@ def test_shared_prefix_equals_private_copies(part):
     assert torch.equal(o1.cpu().view(torch.int16), o2.cpu().view(torch.int16))
 
 
-def _decode(dev, rows, impl, b, out=None):
+def _decode(dev, rows, impl, b, part=0):
     """pa_decode (or pa_decode_valu) of the sequences `rows` (a slice) as
     their own batch, over the full batch's pools."""
     return pa.decode(dev["q"][rows], dev["k_cache"], dev["v_cache"],
                      dev["block_tables"][rows], dev["seq_lens"][rows], scale=b.scale,
-                     impl=impl)
+                     impl=impl, partition_size=part)
 
 
 def test_batch_composition():
     b = wl.make_mixed_step()
     out_full, dev = gpu_step(b)                 # the append, then the whole batch
     valu_full = pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                          dev["seq_lens"], scale=b.scale, impl="valu")
+                          dev["seq_lens"], scale=b.scale, impl="valu", partition_size=512)
     torch.cuda.synchronize()
     subsets = [slice(s, s + 1) for s in (0, 1, 77, 128, 200, 255)] + \
               [slice(0, 100), slice(37, 38 + 90), slice(250, 256)]
     worst = 0.0
     for rows in subsets:
-        got = _decode(dev, rows, "mfma", b)
-        got_v = _decode(dev, rows, "valu", b)
+        got = _decode(dev, rows, "auto", b)
+        got_v = _decode(dev, rows, "valu", b, part=512)
         torch.cuda.synchronize()
-        # the vector kernel: bit for bit
+        # the vector kernel with fixed partitions: bit for bit
         assert torch.equal(got_v.view(torch.int16), valu_full[rows].view(torch.int16)), rows
         # the balanced kernel: within the attention tolerance of the batch's
         # rows and of the oracle
@@ -126,7 +128,7 @@ def test_batch_composition():
     from _gpu import oracle_pools
     kp, vp = oracle_pools(b)
     ref = oracle_out(b, kp, vp, pairs=pairs)
-    got = _decode(dev, slice(37, 38 + 90), "mfma", b)
+    got = _decode(dev, slice(37, 38 + 90), "auto", b)
     full_shape = torch.zeros_like(out_full)
     full_shape[37:38 + 90] = got
     compare(full_shape, ref, pairs=pairs, label="sub-batch vs oracle")

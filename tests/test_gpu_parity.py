@@ -51,12 +51,12 @@ def test_worked_example():
     compare(out, oracle_out(b, kp, vp), label="worked_example")
 
 
-@pytest.mark.parametrize("impl", ["mfma", "valu"])
-def test_mixed_step_full_size(impl):
+@pytest.mark.parametrize("impl,part", [("auto", 0), ("valu", 0), ("valu", 512)])
+def test_mixed_step_full_size(impl, part):
     b = wl.make_mixed_step()
-    out, dev = gpu_step(b, impl=impl)
+    out, dev = gpu_step(b, impl=impl, partition_size=part)
     kp, vp = _check_pools(dev, b)
-    compare(out, oracle_out(b, kp, vp), label=f"mixed_step {impl}")
+    compare(out, oracle_out(b, kp, vp), label=f"mixed_step {impl} part{part}")
 
 
 def test_shared_prefix_copy_on_write():
@@ -78,7 +78,7 @@ def test_long_context_split(bs):
     b = wl.make_long_context(bs)
     dev = wl.to_device(b, "cuda:0")
     ref = oracle_out(b, wl.bits(b.k_cache), wl.bits(b.v_cache))
-    for impl, part in (("mfma", 0), ("mfma", 512), ("valu", 0)):
+    for impl, part in (("auto", 0), ("auto", 512), ("valu", 0), ("valu", 512)):
         out, _ = gpu_step(b, partition_size=part, dev=dev, impl=impl)
         compare(out, ref, label=f"long_context bs{bs} {impl} part{part}")
 
@@ -88,7 +88,7 @@ def test_long_context_split(bs):
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
 
 
-@pytest.mark.parametrize("impl", ["mfma", "valu"])
+@pytest.mark.parametrize("impl", ["auto", "mfma", "valu"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16, 32])
@@ -116,7 +116,7 @@ def test_empty_and_single_token_sequences():
     assert torch.equal(out.float().cpu(), v)
 
 
-@pytest.mark.parametrize("impl", ["mfma", "valu"])
+@pytest.mark.parametrize("impl", ["auto", "mfma", "valu"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_large_values(dtype, impl):
     """V ~ N(0, 64^2): the softmax weights' rounding must not grow with |V|
