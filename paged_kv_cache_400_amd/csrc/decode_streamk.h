@@ -163,8 +163,11 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   const int kh0 = wave % hkv, jw = wave / hkv;
   if (jw >= nwh) return;
   // seq_lens is read kLenBatch x 64 lengths at a time, all loads in flight
-  // together: these scans come before the wave's first K/V load, and one
-  // round trip per 64 lengths kept the memory system idle at the start.
+  // together: these scans come before the wave's first K/V load, so each
+  // round trip delays the whole wave.  The first 256 lengths stay in
+  // registers for the search below (a batch of up to 256 sequences is read
+  // once).  Reading 1,024 at a time saved another 2% on 4,096 short
+  // sequences but cost the mixed step and the long-context batch 1%.
   constexpr int kLenBatch = 4;
   auto load_lens = [&](int b, int (&Lb)[kLenBatch]) {
 #pragma unroll
@@ -173,10 +176,17 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       Lb[k] = j < num_seqs ? seq_lens[j] : 0;
     }
   };
+  int Lb0[kLenBatch];
+  load_lens(0, Lb0);
   int64_t per_head = 0, per_head_tiles = 0;  // units and tiles of all sequences
   for (int b = 0; b < num_seqs; b += 64 * kLenBatch) {
     int Lb[kLenBatch];
-    load_lens(b, Lb);
+    if (b == 0) {
+#pragma unroll
+      for (int k = 0; k < kLenBatch; ++k) Lb[k] = Lb0[k];
+    } else {
+      load_lens(b, Lb);
+    }
 #pragma unroll
     for (int k = 0; k < kLenBatch; ++k) {
       per_head += wave_sum(units_of(Lb[k]));
@@ -197,7 +207,12 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     int64_t urun = 0, trun = 0;
     for (int b = 0; b < num_seqs; b += 64 * kLenBatch) {
       int Lb[kLenBatch];
-      load_lens(b, Lb);
+      if (b == 0) {
+#pragma unroll
+        for (int k = 0; k < kLenBatch; ++k) Lb[k] = Lb0[k];
+      } else {
+        load_lens(b, Lb);
+      }
 #pragma unroll
       for (int k = 0; k < kLenBatch; ++k) {
         const int un = units_of(Lb[k]), tn = tiles_of(Lb[k]);
@@ -275,6 +290,13 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   static_assert(sizeof(float) * G * D <= 2 * TW::kTileBytes, "the result fits the wave's V tiles");
 
   TW tw;
+  // The next sequence's length, first 64 table entries and q rows, fetched
+  // when a segment starts so that the next segment does not begin with
+  // three dependent round trips (4,096 sequences of 16-64 positions: 225 ->
+  // 215 us; no change on the mixed step, whose segments are long).
+  int next_L = 0, next_raw = 0;
+  bool have_next = false, use_next = false;
+  typename TW::QRegs next_q;
 
   int64_t g = g0;
   while (true) {
@@ -287,7 +309,12 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     const int32_t* bt_row = block_tables + (int64_t)s * mb;
 
     tw.init(kc, vc, hkv, kh, vtile);
-    if constexpr (!kGather) tw.load_q(q + row0 * D);
+    if constexpr (!kGather) {
+      if (use_next)
+        tw.qr = next_q;
+      else
+        tw.load_q(q + row0 * D);
+    }
     tw.reset();
     uint32_t gathered = 0;
     auto consume = [&](const uint4 (&kr)[KL], int buf, int t0) {
@@ -306,10 +333,11 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     const int blk_last = (p_end - 1) / BS;
     int blk_base = p_lo / BS;
     bool bad = false;
-    auto load_ids = [&]() {
+    // raw: lane j's table entry blk_base + j (loaded here, or prefetched)
+    auto take_ids = [&](int raw) {
       int id = 0;
       if (blk_base + lane <= blk_last) {
-        id = bt_row[blk_base + lane];
+        id = raw;
         if (id < 0 || id >= nb) {
           bad = true;  // never dereferenced: block 0 is read, the rows become NaN
           id = 0;
@@ -318,7 +346,10 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       bad = __builtin_amdgcn_ballot_w64(bad) != 0;
       return id;
     };
-    int vid = load_ids();
+    auto load_ids = [&]() {
+      return take_ids(blk_base + lane <= blk_last ? bt_row[blk_base + lane] : 0);
+    };
+    int vid = use_next ? take_ids(next_raw) : load_ids();  // a prefetched row starts at block 0
 
     auto issue = [&](uint4 (&kr)[KL], int buf, int j) {
       const int t0 = p_lo + j * kT;
@@ -338,6 +369,13 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 
     uint4 ka[KL], kb[KL];
     issue(ka, 0, 0);
+    have_next = g + ntiles < g1 && s + 1 < num_seqs;  // the run goes on past this sequence
+    if (have_next) {
+      next_L = seq_lens[s + 1];
+      next_raw = lane < mb ? block_tables[(int64_t)(s + 1) * mb + lane] : 0;
+      if constexpr (!kGather)
+        TW::fetch_q(next_q, q + ((int64_t)(s + 1) * hq + (int64_t)kh * G) * D);
+    }
     for (int j = 0;;) {
       wait_vmem_all();
       if (j + 1 < ntiles) issue(kb, 1, j + 1);
@@ -360,39 +398,58 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     // the run goes on, so this sequence ended here: the next one, same head
     t_lo = 0;
     seq_ustart += (ns + pt - 1) / pt;
-    do {
-      if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
-      L = seq_lens[s];
+    use_next = have_next && tiles_of(next_L) > 0;
+    if (use_next) {
+      ++s;
+      L = next_L;
       ns = tiles_of(L);
-    } while (ns == 0);
+    } else {
+      do {
+        if (++s >= num_seqs) return;  // unreachable: tiles remain in the run
+        L = seq_lens[s];
+        ns = tiles_of(L);
+      } while (ns == 0);
+    }
   }
 }
 
 // Merge of the partials of every (sequence, KV head) pair split between
 // waves, plus the rows no wave writes: zero rows for empty sequences, NaN
-// rows for lengths outside [0, max_blocks_per_seq * block_size].  One
-// workgroup per pair; a thread merges 4 consecutive elements of one query
-// head.  The length and the pair's record are loaded together, then the
-// partials four at a time with all their loads in flight at once.
-template <typename T, int D, int G>
+// rows for lengths outside [0, max_blocks_per_seq * block_size].  TPP
+// threads per pair, 256 / TPP pairs per workgroup: 256 when pairs are few
+// (each long pair has many partials, and the more threads merge it the
+// less of their load latency is in series), 64 when they are many (4,096
+// sequences x 8 heads in workgroups of one pair launched 32,768 workgroups,
+// most for pairs no run cut, and the merge took 15 us).  A thread merges 4
+// consecutive elements of one query head at a time.  The length and the
+// pair's record are loaded together, then the partials four at a time with
+// all their loads in flight at once.
+constexpr int kManyPairs = 4096;  // from this many pairs on, one wave per pair
+
+template <typename T, int D, int G, int TPP>
 __global__ void __launch_bounds__(256)
 pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
                   const float2* __restrict__ ws_ml, const int4* __restrict__ ws_meta,
-                  const int32_t* __restrict__ seq_lens, int32_t hkv, int32_t max_len) {
+                  const int32_t* __restrict__ seq_lens, int32_t num_pairs, int32_t hkv,
+                  int32_t max_len) {
+  static_assert(TPP == 64 || TPP == 256, "a wave or a workgroup per pair");
   constexpr int kBatch = 4;
-  const int pair = blockIdx.x;
+  const int lane = threadIdx.x % TPP;
+  const int pair = blockIdx.x * (256 / TPP) + threadIdx.x / TPP;
+  if (pair >= num_pairs) return;
   const int s = pair / hkv, kh = pair % hkv;
   const int64_t row0 = (int64_t)s * hkv * G + (int64_t)kh * G;
   const int L = seq_lens[s];
   const int4 meta = ws_meta[pair];  // meaningful only when L is in range
   if (L <= 0 || L > max_len) {
-    const float v = L == 0 ? 0.0f : __builtin_nanf("");
-    for (int i = threadIdx.x; i < G * D; i += 256) out[row0 * D + i] = to_bits<T>(v);
+    const uint32_t v = L == 0 ? 0u : (uint32_t)to_bits<T>(__builtin_nanf("")) * 0x10001u;
+    for (int i = lane * 8; i < G * D; i += TPP * 8)
+      *reinterpret_cast<uint4*>(out + row0 * D + i) = make_uint4(v, v, v, v);
     return;
   }
   const int c_first = meta.x, c_last = meta.y;
   if (c_first == c_last) return;  // finished by one wave
-  for (int i = threadIdx.x * 4; i < G * D; i += 256 * 4) {
+  for (int i = lane * 4; i < G * D; i += TPP * 4) {
     const int h = i / D, d = i % D;
     float M = kNegInf, den = 0.0f;
     float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -507,9 +564,16 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                      a.out_scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((pa_streamk_reduce<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),
-                     dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
-                     a.seq_lens, a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+  if (pairs >= kManyPairs)
+    hipLaunchKernelGGL((pa_streamk_reduce<T, D, G, 64>), dim3((uint32_t)((pairs + 3) / 4)),
+                       dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
+                       a.seq_lens, (int32_t)pairs, a.num_kv_heads,
+                       a.max_blocks_per_seq * a.block_size);
+  else
+    hipLaunchKernelGGL((pa_streamk_reduce<T, D, G, 256>), dim3((uint32_t)pairs), dim3(256), 0,
+                       a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta, a.seq_lens,
+                       (int32_t)pairs, a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
   return hipGetLastError();
 }
 

@@ -153,7 +153,10 @@ struct TileWave {
   unsigned char* vtile;
   int lane, col, grp;
 
-  uint4 qb[KC];      // q operand (B of q.K^T): head col, d-chunk c*4 + grp
+  struct QRegs {     // q operand (B of q.K^T): head col, d-chunk c*4 + grp
+    uint4 r[KC];
+  };
+  QRegs qr;
   f32x4_t acc[NM];   // P.V accumulators: head 4*grp + r, column 16*m + col
   float m_run;       // running max of head col (same in the 4 lane groups)
   float l_run;       // this lane's share of head col's denominator
@@ -171,13 +174,15 @@ struct TileWave {
   }
 
   // q rows of the G heads start at q_rows ([G][D]); zero operand for col >= G.
-  __device__ __forceinline__ void load_q(const uint16_t* q_rows) {
+  static __device__ __forceinline__ void fetch_q(QRegs& dst, const uint16_t* q_rows) {
+    const int l = threadIdx.x & 63, c16 = l & 15, g4 = l >> 4;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      qb[c] = make_uint4(0u, 0u, 0u, 0u);
-      if (col < G) qb[c] = *reinterpret_cast<const uint4*>(q_rows + col * D + (c * 4 + grp) * 8);
+      dst.r[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (c16 < G) dst.r[c] = *reinterpret_cast<const uint4*>(q_rows + c16 * D + (c * 4 + g4) * 8);
     }
   }
+  __device__ __forceinline__ void load_q(const uint16_t* q_rows) { fetch_q(qr, q_rows); }
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -232,7 +237,7 @@ struct TileWave {
                                           float qk_scale) {
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) sc = mfma_k32<T>(kr[c], qb[c], sc);
+    for (int c = 0; c < KC; ++c) sc = mfma_k32<T>(kr[c], qr.r[c], sc);
 
     float sr[4];
     float lm = kNegInf;

@@ -95,7 +95,10 @@ struct TileWave8 {
   unsigned char* vtile;
   int lane, col, grp;
 
-  uint4 qb[KC];      // q operand, step 2c + h: head col, d = 64c + 16 grp + 8h .. +8
+  struct QRegs {     // q operand, step 2c + h: head col, d = 64c + 16 grp + 8h .. +8
+    uint4 r[KC];
+  };
+  QRegs qr;
   f32x4_t acc[NM];   // P.V accumulators: head 4*grp + r, column 16*m + col
   float m_run;       // running max of head col
   float l_run;       // this lane's share of head col's denominator
@@ -112,18 +115,20 @@ struct TileWave8 {
     grp = lane >> 4;
   }
 
-  __device__ __forceinline__ void load_q(const uint16_t* q_rows) {
+  static __device__ __forceinline__ void fetch_q(QRegs& dst, const uint16_t* q_rows) {
+    const int l = threadIdx.x & 63, c16 = l & 15, g4 = l >> 4;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        qb[2 * c + h] = make_uint4(0u, 0u, 0u, 0u);
-        if (col < G)
-          qb[2 * c + h] =
-              *reinterpret_cast<const uint4*>(q_rows + col * D + 64 * c + 16 * grp + 8 * h);
+        dst.r[2 * c + h] = make_uint4(0u, 0u, 0u, 0u);
+        if (c16 < G)
+          dst.r[2 * c + h] =
+              *reinterpret_cast<const uint4*>(q_rows + c16 * D + 64 * c + 16 * g4 + 8 * h);
       }
     }
   }
+  __device__ __forceinline__ void load_q(const uint16_t* q_rows) { fetch_q(qr, q_rows); }
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -181,8 +186,8 @@ struct TileWave8 {
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const uint4 k8 = kr[u * KCH + c];
-        sc[u] = mfma_k32<T>(widen8<T>(k8.x, k8.y), qb[2 * c], sc[u]);
-        sc[u] = mfma_k32<T>(widen8<T>(k8.z, k8.w), qb[2 * c + 1], sc[u]);
+        sc[u] = mfma_k32<T>(widen8<T>(k8.x, k8.y), qr.r[2 * c], sc[u]);
+        sc[u] = mfma_k32<T>(widen8<T>(k8.z, k8.w), qr.r[2 * c + 1], sc[u]);
       }
     }
 

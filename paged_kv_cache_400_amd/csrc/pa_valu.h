@@ -47,7 +47,7 @@ struct TileWaveV {
   static constexpr int NI = kTileLen / RPL;      // loads per tile, of K and of V each
   static constexpr int KL = 2 * NI;              // kr[0, NI): K, kr[NI, 2 NI): V
   static constexpr int kIds = BS < kTileLen ? kTileLen / BS : 1;
-  static constexpr int kTileBytes = G * D * 2;   // LDS: the result's staging only
+  static constexpr int kTileBytes = G * D * 4;   // LDS: the result's staging only
 
   const uint16_t* kc;
   const uint16_t* vc;
@@ -55,7 +55,10 @@ struct TileWaveV {
   int64_t head_off;    // elements to the KV head within a block
   int lane, row, col;
 
-  uint4 qv[G];         // q of head h, elements 8 col .. 8 col + 7
+  struct QRegs {       // q of head h, elements 8 col .. 8 col + 7
+    uint4 r[G];
+  };
+  QRegs qr;
   float acc[G][8];     // the lane's stream: sum of p V over its 8 elements
   float m[G], l[G];    // the lane's stream: running max and sum
 
@@ -70,10 +73,12 @@ struct TileWaveV {
     col = lane % LPT;
   }
 
-  __device__ __forceinline__ void load_q(const uint16_t* q_rows) {
+  static __device__ __forceinline__ void fetch_q(QRegs& dst, const uint16_t* q_rows) {
+    const int c = (threadIdx.x & 63) % LPT;
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const uint4*>(q_rows + h * D + col * 8);
+    for (int h = 0; h < G; ++h) dst.r[h] = *reinterpret_cast<const uint4*>(q_rows + h * D + c * 8);
   }
+  __device__ __forceinline__ void load_q(const uint16_t* q_rows) { fetch_q(qr, q_rows); }
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -119,10 +124,10 @@ struct TileWaveV {
       valid[i] = t0 + i * RPL + row < t_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float a = dot2<T>(qv[h].x, kr[i].x, 0.0f);
-        a = dot2<T>(qv[h].y, kr[i].y, a);
-        a = dot2<T>(qv[h].z, kr[i].z, a);
-        a = dot2<T>(qv[h].w, kr[i].w, a);
+        float a = dot2<T>(qr.r[h].x, kr[i].x, 0.0f);
+        a = dot2<T>(qr.r[h].y, kr[i].y, a);
+        a = dot2<T>(qr.r[h].z, kr[i].z, a);
+        a = dot2<T>(qr.r[h].w, kr[i].w, a);
         s[i][h] = valid[i] ? group_sum<LPT>(a) * qk_scale : kNegInf;
       }
     }
