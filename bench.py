@@ -154,7 +154,7 @@ def parse():
     ap.add_argument("--kv", choices=["16", "fp8"], default="16",
                     help="16: bf16 pools (the headline); fp8: the same step over 8-bit E4M3 "
                          "pools (pa_reshape_and_cache_fp8 + pa_decode_fp8)")
-    ap.add_argument("--mode", choices=["decode", "prefill", "serve", "long", "groups"],
+    ap.add_argument("--mode", choices=["decode", "prefill", "serve", "long", "groups", "shared"],
                     default="decode",
                     help="decode: the mixed decode step (the headline); prefill: the chunked "
                          "prefill step (32 sequences x 512-token chunks, pa_prefill); serve: "
@@ -618,14 +618,33 @@ def shared_prefix_summary(args):
         pa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                   dev["seq_lens"], scale=b.scale, out=out, workspace=ws)
 
+    # the blocks every table shares (after the copy-on-write: 127 of 128)
+    nblk = min(-(-int(L) // b.block_size) for L in b.seq_lens)
+    pb = 0
+    while pb < nblk and (b.block_tables[:, pb] == b.block_tables[0, pb]).all():
+        pb += 1
+    ws_sp = torch.empty(max(pa.decode_shared_prefix_workspace_bytes(S, Hq, d, pb,
+                                                                     b.block_size), 1),
+                        dtype=torch.uint8, device="cuda:0")
+
+    def decode_shared():
+        pa.decode_shared_prefix(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                dev["seq_lens"], pb, scale=b.scale, out=out, workspace=ws_sp)
+
     def step():
         copy_append()
         decode()
+
+    def step_shared():
+        copy_append()
+        decode_shared()
 
     steps = max(1, min(args.steps, 50))
     ms_step = time_calls(step, steps, args.warmup)
     ms_copy_append = time_calls(copy_append, steps, args.warmup)
     ms_decode = time_calls(decode, steps, args.warmup)
+    ms_step_shared = time_calls(step_shared, steps, args.warmup)
+    ms_shared = time_calls(decode_shared, steps, args.warmup)
     logical, unique = b.kv_bytes(), unique_kv_bytes(b)
     return {
         "workload": SHARED_WORKLOAD + " (cache-warm)",
@@ -636,6 +655,16 @@ def shared_prefix_summary(args):
         "decode_logical_gbs": round(logical / (ms_decode * 1e-3) / 1e9, 2),
         "decode_unique_gbs": round(unique / (ms_decode * 1e-3) / 1e9, 2),
         "decode_seqs_per_s": round(S / (ms_decode * 1e-3), 1),
+        "shared_prefix_decode": {
+            "entry_point": "pa_decode_shared_prefix",
+            "prefix_blocks": pb,
+            "ms_per_step": round(ms_step_shared, 5),
+            "decode_ms": round(ms_shared, 5),
+            "decode_logical_gbs": round(logical / (ms_shared * 1e-3) / 1e9, 2),
+            "decode_unique_gbs": round(unique / (ms_shared * 1e-3) / 1e9, 2),
+            "decode_seqs_per_s": round(S / (ms_shared * 1e-3), 1),
+            "speedup_vs_pa_decode": round(ms_decode / ms_shared, 3),
+        },
     }
 
 
@@ -751,6 +780,22 @@ def groups_line(args):
     }
 
 
+def shared_line(args):
+    """The shared-prefix step as the line's workload (cache-warm): value =
+    logical KV GB/s of pa_decode_shared_prefix; pa_decode on the same step
+    beside it in `shared_prefix`."""
+    sp = shared_prefix_summary(args)
+    row = sp["shared_prefix_decode"]
+    return {
+        "metric": METRIC, "value": row["decode_logical_gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": max(1, min(args.steps, 50)), "warmup": args.warmup,
+        "ms_per_step": row["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": SHARED_WORKLOAD, "kv_bytes": sp["logical_kv_bytes"]},
+        "shared_prefix": sp,
+    }
+
+
 def long_line(args):
     """The long-context batch as the line's workload: value = effective KV
     GB/s of pa_decode (balanced split) at block size 16; every block size
@@ -797,6 +842,9 @@ def main():
         return
     if args.mode == "long":
         print(json.dumps(long_line(args)), flush=True)
+        return
+    if args.mode == "shared":
+        print(json.dumps(shared_line(args)), flush=True)
         return
 
     b = wl.make_mixed_step(kv=args.kv)

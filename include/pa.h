@@ -163,6 +163,49 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                             pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_decode for a batch whose sequences share a prefix: the first
+ * prefix_blocks entries of every sequence's block table are the same
+ * physical blocks (a shared system prompt, the candidates of a beam search:
+ * "What problem does PagedAttention solve, and what is continuous
+ * batching?", section "How PagedAttention works"; "PagedAttention &
+ * Continuous Batching", section "Production defaults", prefix caching).
+ * The result is pa_decode's (to float32 rounding): softmax attention of each
+ * q[s][h] over positions 0..L_s-1.  The work is split at position
+ * P = prefix_blocks * block_size: the prefix is attended once for all the
+ * batch's query rows together (16 (sequence, head) rows per matrix-core
+ * product, so each prefix block is read for 16 rows at a time rather than
+ * once per sequence), each sequence's positions [P, L_s) by pa_decode's
+ * balanced split, and the two are merged by log-sum-exp.
+ *
+ * Contract: every sequence has P <= seq_lens[s] <= max_blocks_per_seq *
+ * block_size and block_tables[s][j] == block_tables[0][j] for j <
+ * prefix_blocks; a sequence that breaks it gets NaN rows (the others are
+ * unaffected).  prefix_blocks = 0 is pa_decode (partition_size 0).  Other
+ * arguments, supported sizes and errors as pa_decode; prefix_blocks outside
+ * [0, max_blocks_per_seq] is PA_ERR_SHAPE.  The workspace needs
+ * pa_decode_shared_prefix_workspace_bytes(...) bytes (16-byte aligned).
+ * Three kernels run in order on `stream`.
+ */
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t num_blocks, int32_t prefix_blocks, float scale,
+                                  pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * Workspace bytes of pa_decode_shared_prefix on the current device: pa_decode's
+ * balanced-split workspace, plus (m, l, acc) float32 per (sequence, query
+ * head) for the tails and for each 128-position chunk of the prefix.  0 when
+ * an argument is invalid.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t prefix_blocks,
+                                               int32_t block_size);
+
+/*
  * pa_decode computed on the vector unit alone instead of the matrix cores:
  * q.K as packed dot products reduced across the lanes of a row (DPP), the
  * online softmax per lane, P.V as float32 FMAs with the weights kept in

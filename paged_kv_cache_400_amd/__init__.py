@@ -5,7 +5,8 @@ of ``include/pa.h``); :mod:`.binding` is its Python binding.  Importing this
 package does not load the library; the first use of one of its names does,
 and fails loudly if it has not been built.
 """
-_BINDING_NAMES = ("decode", "decode_noalloc", "reshape_and_cache", "copy_blocks",
+_BINDING_NAMES = ("decode", "decode_noalloc", "decode_shared_prefix",
+                  "decode_shared_prefix_workspace_bytes", "reshape_and_cache", "copy_blocks",
                   "decode_workspace_bytes", "decode_fp8", "reshape_and_cache_fp8", "prefill",
                   "probe_gather", "probe_stream", "BlockManager", "NoBlocks", "PaError",
                   "abi_version", "LIB_PATH")

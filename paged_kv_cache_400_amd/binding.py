@@ -34,6 +34,10 @@ SIGNATURES = {
     "pa_probe_decode_mfma": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
                                             _vp, _sz, _vp]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _f32,
+                                               ctypes.c_int, _vp, _sz, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_valu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -205,6 +209,54 @@ def decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, out, scale=None,
                                   block_tables.shape[1], NB, float(scale), int(partition_size),
                                   _DT[q.dtype], _stream(dev)))
     return out
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, prefix_blocks, scale=None,
+                         out=None, workspace=None):
+    """pa_decode_shared_prefix: decode of sequences whose block tables all
+    start with the same ``prefix_blocks`` physical blocks; the prefix is
+    attended once for all of them, the tails per sequence, merged by
+    log-sum-exp.  Same tensors as :func:`decode`."""
+    _need(q, "q", 3)
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    _need(k_cache, "k_cache", 4, q.dtype, dev)
+    _need(v_cache, "v_cache", 4, q.dtype, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(seq_lens, "seq_lens", 1, torch.int32, dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    S, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("inconsistent shapes between q, the pools, block_tables and seq_lens")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", 3, q.dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = int(_lib.pa_decode_shared_prefix_workspace_bytes(S, Hq, d, int(prefix_blocks), bs))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None, None, dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_shared_prefix(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, d, bs,
+                                        block_tables.shape[1], NB, int(prefix_blocks),
+                                        float(scale), _DT[q.dtype], _ptr(workspace), ws_bytes,
+                                        _stream(dev)))
+    return out
+
+
+def decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim, prefix_blocks,
+                                         block_size) -> int:
+    return int(_lib.pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                            prefix_blocks, block_size))
 
 
 def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale=None, out=None):

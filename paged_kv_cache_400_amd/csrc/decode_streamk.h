@@ -61,7 +61,7 @@ namespace {
 
 constexpr int kWaves = 4;              // waves per workgroup (independent)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMinChunk = 8;           // tiles per wave at least
+constexpr int kMinChunk = 4;           // tiles per wave at least
 
 // Workgroups per CU the launch uses: two (8 waves), not the three that fit.
 // The K/V gather saturates with as few as 4 waves per CU (the gather-only
@@ -131,7 +131,8 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   const int32_t* __restrict__ block_tables,
                   const int32_t* __restrict__ seq_lens, int32_t num_seqs, int32_t hkv,
                   int32_t mb, int32_t nb, int32_t nwaves, int32_t part_tiles, float qk_scale,
-                  float out_scale) {
+                  float out_scale, int32_t start, float* __restrict__ pair_acc,
+                  float2* __restrict__ pair_ml) {
   using TW = typename TileWaveOf<T, KV, D, BS, G>::type;
   constexpr int KL = TW::KL, kT = TW::kTileLen, kIds = TW::kIds;
   constexpr bool kScaled = std::is_same<KV, FP8>::value;
@@ -145,8 +146,11 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   const int wave = blockIdx.x * kWaves + w;
   const int hq = hkv * G;
   const int64_t max_len = (int64_t)mb * BS;
+  // Positions [start, L) of each sequence are walked (start = 0 but for the
+  // tails of pa_decode_shared_prefix, whose first `start` positions are a
+  // prefix attended separately).
   auto tiles_of = [&](int L) -> int {
-    return (L > 0 && (int64_t)L <= max_len) ? (L + kT - 1) / kT : 0;
+    return (L > start && (int64_t)L <= max_len) ? (L - start + kT - 1) / kT : 0;
   };
 
   // ---- this wave's run: wave w works on KV head w % hkv, and the waves of
@@ -263,9 +267,16 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                           int t_hi, int ns, bool first, int64_t pair_ustart) {
     const bool whole = t_lo == 0 && t_hi == ns;
     float* st = reinterpret_cast<float*>(vtile);  // [G][D]
-    t.stage(st, whole, bad, kScaled ? out_scale : 1.0f);
+    t.stage(st, whole && pair_acc == nullptr, bad, kScaled ? out_scale : 1.0f);
     // one wave's LDS accesses take effect in program order
-    if (whole) {
+    if (whole && pair_acc != nullptr) {
+      // a shared-prefix tail: the whole pair's state, for the merge with the prefix
+      for (int i = lane * 4; i < G * D; i += 64 * 4)
+        *reinterpret_cast<float4*>(pair_acc + row0 * D + i) =
+            *reinterpret_cast<const float4*>(st + i);
+      const float2 ml = t.ml_of_lane();
+      if (lane < G) pair_ml[row0 + lane] = make_float2(ml.x, bad ? __builtin_nanf("") : ml.y);
+    } else if (whole) {
       for (int i = lane * 8; i < G * D; i += 64 * 8) {
         const float4 a = *reinterpret_cast<const float4*>(st + i);
         const float4 b = *reinterpret_cast<const float4*>(st + i + 4);
@@ -292,18 +303,19 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   TW tw;
   // The next sequence's length, first 64 table entries and q rows, fetched
   // when a segment starts so that the next segment does not begin with
-  // three dependent round trips (4,096 sequences of 16-64 positions: 225 ->
-  // 215 us; no change on the mixed step, whose segments are long).
+  // three dependent round trips.  All initialised: a register left undefined
+  // on some path can make the compiler wait for every outstanding load when
+  // it copies that register inside the tile loop.
   int next_L = 0, next_raw = 0;
   bool have_next = false, use_next = false;
-  typename TW::QRegs next_q;
+  typename TW::QRegs next_q{};
 
   int64_t g = g0;
   while (true) {
     // ---- one segment: pair (s, kh), tiles [t_lo, t_hi)
     const int t_hi = (int)min((int64_t)ns, (int64_t)t_lo + (g1 - g));
-    const int p_lo = t_lo * kT;
-    const int p_end = min(L, t_hi * kT);  // positions [p_lo, p_end)
+    const int p_lo = start + t_lo * kT;
+    const int p_end = min(L, start + t_hi * kT);  // positions [p_lo, p_end)
     const int ntiles = t_hi - t_lo;
     const int64_t row0 = (int64_t)s * hq + (int64_t)kh * G;
     const int32_t* bt_row = block_tables + (int64_t)s * mb;
@@ -319,11 +331,10 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     uint32_t gathered = 0;
     auto consume = [&](const uint4 (&kr)[KL], int buf, int t0) {
       if constexpr (kGather) {
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes);
         // every loaded K word enters the XOR, or the compiler narrows the loads
 #pragma unroll
         for (int c = 0; c < KL; ++c) gathered ^= kr[c].x ^ kr[c].y ^ kr[c].z ^ kr[c].w;
-        gathered ^= vw[lane];
+        gathered ^= reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes)[lane];
       } else {
         tw.consume(kr, buf, t0, p_end, qk_scale);
       }
@@ -349,7 +360,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     auto load_ids = [&]() {
       return take_ids(blk_base + lane <= blk_last ? bt_row[blk_base + lane] : 0);
     };
-    int vid = use_next ? take_ids(next_raw) : load_ids();  // a prefetched row starts at block 0
+    int vid = use_next ? take_ids(next_raw) : load_ids();  // prefetched from block start / BS
 
     auto issue = [&](uint4 (&kr)[KL], int buf, int j) {
       const int t0 = p_lo + j * kT;
@@ -372,19 +383,36 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     have_next = g + ntiles < g1 && s + 1 < num_seqs;  // the run goes on past this sequence
     if (have_next) {
       next_L = seq_lens[s + 1];
-      next_raw = lane < mb ? block_tables[(int64_t)(s + 1) * mb + lane] : 0;
+      const int b0 = start / BS;  // the next segment's first block
+      next_raw = b0 + lane < mb ? block_tables[(int64_t)(s + 1) * mb + b0 + lane] : 0;
       if constexpr (!kGather)
         TW::fetch_q(next_q, q + ((int64_t)(s + 1) * hq + (int64_t)kh * G) * D);
     }
-    for (int j = 0;;) {
+    // Tile j + 1 goes into the other buffer once the wave has waited for
+    // everything: one tile in flight per wave while it computes.  Issuing it
+    // before the wait (two in flight while the wave waits; possible for the
+    // tile waves whose loads the compiler counts exactly) took 3% off 4,096
+    // short sequences but cost the bandwidth-bound batches 1.5-2.5%: more
+    // scattered requests outstanding per CU than the memory system serves
+    // well.  Done only on short segments, it left the compiler copies of
+    // undefined loop values that made it wait for all loads anyway.
+    auto next = [&](uint4 (&kn)[KL], int buf, int jn) {
       wait_vmem_all();
-      if (j + 1 < ntiles) issue(kb, 1, j + 1);
+      if (jn < ntiles) issue(kn, buf, jn);
+    };
+    // Tiles in pairs, the loop's only exit at its top: a loop left from its
+    // middle gave the compiler undefined loop values to copy, and the copy
+    // of an undefined register made it wait for every outstanding load.
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+      next(kb, 1, j + 1);
       consume(ka, 0, p_lo + j * kT);
-      if (++j >= ntiles) break;
-      wait_vmem_all();
-      if (j + 1 < ntiles) issue(ka, 0, j + 1);
-      consume(kb, 1, p_lo + j * kT);
-      if (++j >= ntiles) break;
+      next(ka, 0, j + 2);
+      consume(kb, 1, p_lo + (j + 1) * kT);
+    }
+    if (j < ntiles) {
+      next(kb, 1, j + 1);
+      consume(ka, 0, p_lo + j * kT);
     }
     if constexpr (kGather) {
       if (gathered == 0x9e3779b9u && lane == 0) out[0] = (uint16_t)gathered;
@@ -492,6 +520,116 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
   }
 }
 
+// The merge of pa_decode_shared_prefix, one workgroup per (sequence, KV
+// head) pair: the prefix's chunk partials (pre_*, rows [chunk][S * Hq]) and
+// the tail's state (the pair buffer when one wave finished the tail, else
+// the waves' slots named by the pair's record), folded four at a time by
+// log-sum-exp in that order.  A sequence shorter than the prefix, longer
+// than its table, or whose table's first prefix_blocks entries differ from
+// sequence 0's breaks the contract: NaN rows.  One with no positions past
+// the prefix takes the prefix's result alone.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+pa_prefix_merge(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
+                const float2* __restrict__ ws_ml, const int4* __restrict__ ws_meta,
+                const float* __restrict__ pair_acc, const float2* __restrict__ pair_ml,
+                const float* __restrict__ pre_acc, const float2* __restrict__ pre_ml,
+                const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_tables,
+                int32_t num_seqs, int32_t hkv, int32_t mb, int32_t max_len, int32_t start,
+                int32_t prefix_blocks, int32_t nchunks) {
+  constexpr int kBatch = 4;
+  const int pair = blockIdx.x;
+  const int s = pair / hkv, kh = pair % hkv;
+  const int64_t rows = (int64_t)num_seqs * hkv * G;  // rows of one chunk's partials
+  const int64_t row0 = (int64_t)s * hkv * G + (int64_t)kh * G;
+  const int L = seq_lens[s];
+  const int4 meta = ws_meta[pair];  // meaningful only when the tail was walked
+  int differs = 0;
+  for (int j = threadIdx.x; j < prefix_blocks; j += 256)
+    differs |= block_tables[(int64_t)s * mb + j] != block_tables[j];
+  differs = __syncthreads_or(differs);
+  if (differs || L < start || L > max_len) {
+    const uint32_t v = (uint32_t)to_bits<T>(__builtin_nanf("")) * 0x10001u;
+    for (int i = threadIdx.x * 8; i < G * D; i += 256 * 8)
+      *reinterpret_cast<uint4*>(out + row0 * D + i) = make_uint4(v, v, v, v);
+    return;
+  }
+  const bool tail = L > start, split = tail && meta.x != meta.y;
+  const int n = nchunks + (!tail ? 0 : split ? meta.y - meta.x + 1 : 1);
+  for (int i = threadIdx.x * 4; i < G * D; i += 256 * 4) {
+    const int h = i / D, d = i % D;
+    auto source = [&](int k, float2& ml, float4& a) {
+      if (k < nchunks) {
+        const int64_t r = (int64_t)k * rows + row0 + h;
+        ml = pre_ml[r];
+        a = *reinterpret_cast<const float4*>(pre_acc + r * D + d);
+      } else if (!split) {
+        ml = pair_ml[row0 + h];
+        a = *reinterpret_cast<const float4*>(pair_acc + (row0 + h) * D + d);
+      } else {
+        const int c = meta.x + (k - nchunks);
+        const int64_t slot = 2 * ((int64_t)c * hkv + kh) + (c == meta.x ? meta.z : 0);
+        ml = ws_ml[slot * G + h];
+        a = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
+      }
+    };
+    float M = kNegInf, den = 0.0f;
+    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < n; k0 += kBatch) {
+      float2 ml[kBatch];
+      float4 a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        ml[u] = make_float2(kNegInf, 0.0f);
+        a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (k0 + u < n) source(k0 + u, ml[u], a[u]);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
+      const float base = (Mb == kNegInf) ? 0.0f : Mb;
+      const float r = exp2_fast(M - base);
+      den *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] *= r;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float f = exp2_fast(ml[u].x - base);
+        den = fmaf(f, ml[u].y, den);
+        num[0] = fmaf(f, a[u].x, num[0]);
+        num[1] = fmaf(f, a[u].y, num[1]);
+        num[2] = fmaf(f, a[u].z, num[2]);
+        num[3] = fmaf(f, a[u].w, num[3]);
+      }
+      M = Mb;
+    }
+    *reinterpret_cast<uint2*>(out + (row0 + h) * D + d) =
+        make_uint2(pack2<T>(num[0] / den, num[1] / den), pack2<T>(num[2] / den, num[3] / den));
+  }
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_prefix_merge_t(const PrefixArgs& a) {
+  hipLaunchKernelGGL((pa_prefix_merge<T, D, G>), dim3((uint32_t)a.num_seqs * a.num_kv_heads),
+                     dim3(256), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
+                     a.pair_acc, a.pair_ml, a.pre_acc, a.pre_ml, a.seq_lens, a.block_tables,
+                     a.num_seqs, a.num_kv_heads, a.max_blocks_per_seq,
+                     a.max_blocks_per_seq * a.block_size, a.prefix_blocks * a.block_size,
+                     a.prefix_blocks, (int32_t)prefix_chunks(a.prefix_blocks, a.block_size));
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_prefix_merge_d(const PrefixArgs& a) {
+  switch (a.group) {
+    case 1: return launch_prefix_merge_t<T, D, 1>(a);
+    case 2: return launch_prefix_merge_t<T, D, 2>(a);
+    case 4: return launch_prefix_merge_t<T, D, 4>(a);
+    case 8: return launch_prefix_merge_t<T, D, 8>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------------------
 
 // Waves of one decode launch on the current device: kWorkgroupsPerCu
@@ -549,7 +687,8 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                          dim3(kThreads), 0, a.stream, (uint16_t*)a.out, nullptr, nullptr,
                          nullptr, nullptr, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                          a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
-                         a.max_blocks_per_seq, a.num_blocks, waves, 0, 0.0f, 0.0f);
+                         a.max_blocks_per_seq, a.num_blocks, waves, 0, 0.0f, 0.0f, 0, nullptr,
+                         nullptr);
       return hipGetLastError();
     }
   } else {
@@ -561,9 +700,9 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                      (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
                      a.block_tables, a.seq_lens, a.num_seqs, a.num_kv_heads,
                      a.max_blocks_per_seq, a.num_blocks, waves, a.part_tiles, a.qk_scale,
-                     a.out_scale);
+                     a.out_scale, a.start, a.pair_acc, a.pair_ml);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.merge) return e;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
   if (pairs >= kManyPairs)
     hipLaunchKernelGGL((pa_streamk_reduce<T, D, G, 64>), dim3((uint32_t)((pairs + 3) / 4)),

@@ -18,6 +18,12 @@ hipError_t launch_gather_streamk(const StreamKArgs& a) {
   return a.bf16 ? launch_d<BF16, BF16>(a, true) : launch_d<F16, F16>(a, true);
 }
 
+hipError_t launch_prefix_merge(const PrefixArgs& a) {
+  if (a.head_dim == 64) return a.bf16 ? launch_prefix_merge_d<BF16, 64>(a)
+                                      : launch_prefix_merge_d<F16, 64>(a);
+  return a.bf16 ? launch_prefix_merge_d<BF16, 128>(a) : launch_prefix_merge_d<F16, 128>(a);
+}
+
 int streamk_device_waves() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

@@ -331,6 +331,136 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                      1.0f, true);
 }
 
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t prefix_blocks,
+                                               int32_t block_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || prefix_blocks < 0 ||
+      block_size <= 0)
+    return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const int64_t sk = pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                 pa::streamk_device_waves());
+  if (prefix_blocks == 0) return (size_t)sk;
+  const int64_t nch = pa::prefix_chunks(prefix_blocks, block_size);
+  return (size_t)(sk + (1 + nch) * rows * ((int64_t)head_dim * 4 + 8));
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t num_blocks, int32_t prefix_blocks, float scale,
+                                  pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (prefix_blocks < 0 || (max_blocks_per_seq > 0 && prefix_blocks > max_blocks_per_seq))
+    return fail(PA_ERR_SHAPE,
+                "pa_decode_shared_prefix: prefix_blocks %d must be in [0, max_blocks_per_seq %d]",
+                prefix_blocks, max_blocks_per_seq);
+  if (prefix_blocks == 0)  // nothing shared: the plain decode
+    return decode_impl(Impl::kAuto, out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                       num_blocks, scale, 0, dtype, workspace, workspace_bytes, stream);
+  // the same validation as pa_decode, with no work launched: a zero-sized call
+  const pa_status st = decode_impl(Impl::kAuto, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, 0, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, 0, dtype, nullptr, 0,
+                                   stream);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (num_seqs < 0)
+    return fail(PA_ERR_SHAPE, "pa_decode_shared_prefix: num_seqs %d is negative", num_seqs);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "pa_decode_shared_prefix: a required pointer is NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_SHAPE,
+                "pa_decode_shared_prefix: out, q, k_cache and v_cache must be 16-byte aligned");
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const int64_t nch = pa::prefix_chunks(prefix_blocks, block_size);
+  const int64_t prefix_waves = (int64_t)num_kv_heads * ((rows / num_kv_heads + 15) / 16) * nch;
+  if (prefix_waves * 64 >= kMaxThreadsPerLaunch || (int64_t)num_seqs * num_kv_heads >= INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_decode_shared_prefix: too many rows for one launch");
+  const size_t need = pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                             prefix_blocks, block_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "pa_decode_shared_prefix: workspace of %zu bytes needed, %zu "
+                "given%s", need, workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "pa_decode_shared_prefix: workspace must be 16-byte aligned");
+
+  // workspace: the balanced split's (acc, ml, records), then the tails'
+  // whole-pair states (acc, ml), then the prefix's chunk partials (acc, ml)
+  const int waves = pa::streamk_device_waves();
+  char* ws = (char*)workspace;
+  pa::StreamKArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.ws_acc = (float*)ws;
+  a.ws_ml = (float2*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim, waves));
+  a.ws_meta = (int4*)(ws + pa::streamk_acc_bytes(num_q_heads, head_dim, waves) +
+                      pa::streamk_ml_bytes(num_q_heads, waves));
+  a.max_waves = waves;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.part_tiles = 0;
+  a.qk_scale = scale * 1.4426950408889634f;
+  a.out_scale = 1.0f;
+  a.bf16 = dtype == PA_BF16;
+  a.stream = stream;
+  char* p = ws + pa::streamk_workspace_bytes(num_seqs, num_q_heads, head_dim, waves);
+  a.pair_acc = (float*)p;
+  p += rows * head_dim * 4;
+  a.pair_ml = (float2*)p;
+  p += rows * 8;
+  a.start = prefix_blocks * block_size;
+  a.merge = false;
+
+  pa::PrefixArgs b;
+  b.out = out;
+  b.q = q;
+  b.k_cache = k_cache;
+  b.v_cache = v_cache;
+  b.block_tables = block_tables;
+  b.seq_lens = seq_lens;
+  b.pre_acc = (float*)p;
+  p += nch * rows * head_dim * 4;
+  b.pre_ml = (float2*)p;
+  b.ws_acc = a.ws_acc;
+  b.ws_ml = a.ws_ml;
+  b.ws_meta = a.ws_meta;
+  b.pair_acc = a.pair_acc;
+  b.pair_ml = a.pair_ml;
+  b.num_seqs = num_seqs;
+  b.num_kv_heads = num_kv_heads;
+  b.group = group;
+  b.head_dim = head_dim;
+  b.block_size = block_size;
+  b.max_blocks_per_seq = max_blocks_per_seq;
+  b.num_blocks = num_blocks;
+  b.prefix_blocks = prefix_blocks;
+  b.qk_scale = a.qk_scale;
+  b.bf16 = a.bf16;
+  b.stream = stream;
+
+  const char* fn = "pa_decode_shared_prefix";
+  pa_status r = launch_status(fn, pa::launch_prefix_attend(b));
+  if (r != PA_OK) return r;
+  r = launch_status(fn, group == 1 ? pa::launch_decode_streamk_valu(a)
+                                   : pa::launch_decode_streamk(a));
+  if (r != PA_OK) return r;
+  return launch_status(fn, pa::launch_prefix_merge(b));
+}
+
 pa_status pa_decode_valu(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -90,6 +90,14 @@ struct StreamKArgs {
   float out_scale;    // v_scale for 8-bit pools (unused for 16-bit pools)
   bool bf16;          // q and out bf16 (else fp16)
   hipStream_t stream;
+  // pa_decode_shared_prefix's tails: positions [start, L) only; a pair one
+  // wave finishes leaves its state in pair_acc / pair_ml ([S * Hq] rows)
+  // instead of writing out, and the merge is launched separately
+  // (launch_prefix_merge).  0 / null / true for every other caller.
+  int32_t start = 0;
+  float* pair_acc = nullptr;
+  float2* pair_ml = nullptr;
+  bool merge = true;
 };
 
 // Waves a balanced decode launch has on the current device (two workgroups
@@ -114,6 +122,38 @@ inline int64_t streamk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 hipError_t launch_decode_streamk(const StreamKArgs& a);
+
+// pa_decode_shared_prefix (prefix.hip, decode_streamk.hip): the prefix's
+// attention for every (sequence, query head) row, per chunk of
+// kPrefixChunk positions, as partial states pre_acc [nchunks][S * Hq][D] and
+// pre_ml [nchunks][S * Hq]; then, after the tails (launch_decode_streamk
+// with start and pair buffers), the merge of prefix and tail into out.
+constexpr int kPrefixChunk = 128;
+struct PrefixArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* pre_acc;
+  float2* pre_ml;
+  const float* ws_acc;   // the tails' split partials, as StreamKArgs
+  const float2* ws_ml;
+  const int4* ws_meta;
+  const float* pair_acc; // the tails' whole-pair states
+  const float2* pair_ml;
+  int32_t num_seqs, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq, num_blocks, prefix_blocks;
+  float qk_scale;
+  bool bf16;
+  hipStream_t stream;
+};
+inline int64_t prefix_chunks(int32_t prefix_blocks, int32_t block_size) {
+  return ((int64_t)prefix_blocks * block_size + kPrefixChunk - 1) / kPrefixChunk;
+}
+hipError_t launch_prefix_attend(const PrefixArgs& a);
+hipError_t launch_prefix_merge(const PrefixArgs& a);
 // The same split with the vector-unit tile wave (pa_valu.h), 16-bit pools.
 hipError_t launch_decode_streamk_valu(const StreamKArgs& a);
 // Gather-only run of the same split and loads (pa_probe_gather); uses only

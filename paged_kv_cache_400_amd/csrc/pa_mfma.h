@@ -94,6 +94,19 @@ __device__ __forceinline__ void wait_vmem_all() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt not waited for): the wave's vector
+// memory operations but the N most recent have completed.  They complete
+// in the order they were issued, so with the N loads of the tiles issued
+// after tile j still in flight, this waits for tile j, its V copies into LDS
+// included (which only this wait orders before the reads of V).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+  asm volatile("" ::: "memory");
+}
+
 // The G x D result of a matrix-core tile wave, row-major into st: lane (col,
 // grp) holds acc[m][r] for head 4 grp + r, column 16 m + col, and head col's
 // whole denominator in l_run (after finish).  whole: divide by the
@@ -116,6 +129,44 @@ __device__ __forceinline__ void stage_mfma_result(float* st, const f32x4_t (&acc
         st[h * D + 16 * m + col] = bad ? __builtin_nanf("") : v;
       }
     }
+  }
+}
+
+// The NM transpose reads of a V tile for one lane (column block m at byte
+// offset 32 m from the lane's LDS address a), as one asm block that waits for
+// its own results before it ends.  Written as builtins, these reads would
+// make the compiler wait first for every LDS copy the wave has in flight (it
+// cannot tell the buffers apart), the next tiles' copies included; a driver
+// that keeps several tiles in flight must not lose them there.  The
+// caller's own vmcnt wait orders the reads after this tile's copies.
+template <int NM>
+__device__ __forceinline__ void read_v_tr(uint2 (&w)[NM], uint32_t a) {
+  static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
+  if constexpr (NM == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
+          "=&v"(w[6]), "=&v"(w[7])
+        : "v"(a)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+        : "v"(a)
+        : "memory");
   }
 }
 
@@ -232,7 +283,14 @@ struct TileWave {
   }
 
   // Compute the tile at t0 (positions >= t_end masked) whose K is in kr and
-  // V in LDS buffer `buf`.
+  // V in LDS buffer `buf`.  kDrain: wait for every load the wave has in
+  // flight before reading V, the next tile's included.  The decode drivers
+  // keep one tile in flight and drain: with the next tile's loads kept in
+  // flight through P.V instead, the bandwidth-bound batches ran 0.3-0.5%
+  // slower (more scattered requests outstanding than the memory system
+  // serves well).  A driver that keeps several tiles in flight and waits for
+  // each with wait_vmem_but does not drain.
+  template <bool kDrain = true>
   __device__ __forceinline__ void consume(const uint4 (&kr)[KC], int buf, int t0, int t_end,
                                           float qk_scale) {
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -273,15 +331,14 @@ struct TileWave {
     // within each group of 16 lanes: lanes 4r .. 4r + 3 give row r (columns
     // 16 m .. 16 m + 15, 4 each) and lane col receives element col of every
     // row.
-    typedef short i16x4_t2 __attribute__((ext_vector_type(4)));
     const unsigned char* vb = vtile + buf * GE::TILE + grp * GE::REGION + (col >> 2) * GE::ROW +
                               8 * (col & 3);
+    uint2 w[NM];
+    if constexpr (kDrain) wait_vmem_all();
+    read_v_tr<NM>(w, (uint32_t)(uintptr_t)vb);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t2*)(vb + 32 * m)));
-      acc[m] = mfma_k32<T>(pa_op, make_uint4(w.x, w.y, w.x, w.y), acc[m]);
-    }
+    for (int m = 0; m < NM; ++m)
+      acc[m] = mfma_k32<T>(pa_op, make_uint4(w[m].x, w[m].y, w[m].x, w[m].y), acc[m]);
   }
 
   // After the last tile: every lane holds head col's whole denominator.

@@ -73,6 +73,41 @@ template <typename T> __device__ __forceinline__ uint4 widen8(uint32_t w0, uint3
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// The NM byte-transpose reads of an 8-bit V tile for one lane (column block
+// m at byte offset 16 m from a), as one asm block that waits for its own
+// results, for the reason given at read_v_tr: builtins would make the
+// compiler wait for every LDS copy in flight, the next tiles' included.
+template <int NM>
+__device__ __forceinline__ void read_v_tr8(uint2 (&w)[NM], uint32_t a) {
+  static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
+  if constexpr (NM == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8\n\t"
+        "ds_read_b64_tr_b8 %1, %8 offset:16\n\t"
+        "ds_read_b64_tr_b8 %2, %8 offset:32\n\t"
+        "ds_read_b64_tr_b8 %3, %8 offset:48\n\t"
+        "ds_read_b64_tr_b8 %4, %8 offset:64\n\t"
+        "ds_read_b64_tr_b8 %5, %8 offset:80\n\t"
+        "ds_read_b64_tr_b8 %6, %8 offset:96\n\t"
+        "ds_read_b64_tr_b8 %7, %8 offset:112\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
+          "=&v"(w[6]), "=&v"(w[7])
+        : "v"(a)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:16\n\t"
+        "ds_read_b64_tr_b8 %2, %4 offset:32\n\t"
+        "ds_read_b64_tr_b8 %3, %4 offset:48\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+        : "v"(a)
+        : "memory");
+  }
+}
+
 template <typename T, int D, int BS, int G>
 struct TileWave8 {
   using GE = Geo8<D>;
@@ -235,14 +270,14 @@ struct TileWave8 {
     // ds_read_b64_tr_b8 transposes within each group of 16 lanes: lanes 2j
     // and 2j + 1 give the two 8-byte halves of row j (columns 16 m ..
     // 16 m + 15) and lane col receives byte col of every row.
-    typedef int i32x2_t __attribute__((ext_vector_type(2)));
     const unsigned char* vb =
         vtile + buf * GE::TILE + grp * GE::REGION + (col >> 1) * GE::ROW + 8 * (col & 1);
+    uint2 w[NM];
+    wait_vmem_all();  // as TileWave's consume with kDrain
+    read_v_tr8<NM>(w, (uint32_t)(uintptr_t)vb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * m));
-      const uint4 vop = widen8<T>((uint32_t)w.x, (uint32_t)w.y);
+      const uint4 vop = widen8<T>(w[m].x, w[m].y);
       acc[m] = mfma_k32<T>(pa_hi, vop, acc[m]);
       acc[m] = mfma_k32<T>(pa_lo, vop, acc[m]);
     }
