@@ -121,7 +121,11 @@ struct TileWaveOf<T, Vec, D, BS, G> {
 // (kWorkgroupsPerCu), so the compiler may take up to 256 registers; the
 // 8-bit tile wave uses 190 of them (with the 168 that three waves allow it
 // spent 8% more time on the mixed step), the 16-bit one about 150.
-template <typename T, int D, int BS, int G, bool kGather, typename KV>
+//
+// kDeep: one workgroup per CU instead of two, each wave with two tiles in
+// flight instead of one (the 16-bit matrix-core tile wave only, whose loads
+// the compiler counts exactly; see the walk below).
+template <typename T, int D, int BS, int G, bool kGather, typename KV, bool kDeep = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   float2* __restrict__ ws_ml, int4* __restrict__ ws_meta,
@@ -136,6 +140,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   using TW = typename TileWaveOf<T, KV, D, BS, G>::type;
   constexpr int KL = TW::KL, kT = TW::kTileLen, kIds = TW::kIds;
   constexpr bool kScaled = std::is_same<KV, FP8>::value;
+  static_assert(!kDeep || std::is_same<KV, T>::value, "kDeep: the 16-bit matrix-core tile wave");
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * TW::kTileBytes];
   static_assert(sizeof(s_mem) <= kMaxLdsBytes, "one workgroup's LDS fits gfx950's 160 KiB");
   static_assert(kWorkgroupsPerCu * sizeof(s_mem) <= kMaxLdsBytes,
@@ -334,7 +339,12 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
         // every loaded K word enters the XOR, or the compiler narrows the loads
 #pragma unroll
         for (int c = 0; c < KL; ++c) gathered ^= kr[c].x ^ kr[c].y ^ kr[c].z ^ kr[c].w;
-        gathered ^= reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes)[lane];
+        if constexpr (kDeep)
+          gathered ^= lds_read_u32((uint32_t)(uintptr_t)(vtile + buf * TW::kTileBytes) + 4 * lane);
+        else
+          gathered ^= reinterpret_cast<const uint32_t*>(vtile + buf * TW::kTileBytes)[lane];
+      } else if constexpr (kDeep) {
+        tw.template consume<false>(kr, buf, t0, p_end, qk_scale);
       } else {
         tw.consume(kr, buf, t0, p_end, qk_scale);
       }
@@ -375,7 +385,10 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 #pragma unroll
       for (int i = 1; i < kIds; ++i)
         ids[i] = (t0 + i * BS < p_end) ? __builtin_amdgcn_readlane(vid, b + i) : ids[0];
-      tw.issue_ids(kr, buf, t0, p_end - 1, ids);
+      if constexpr (kDeep)
+        tw.issue_ids_counted(kr, buf, t0, p_end - 1, ids);
+      else
+        tw.issue_ids(kr, buf, t0, p_end - 1, ids);
     };
 
     uint4 ka[KL], kb[KL];
@@ -388,17 +401,27 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       if constexpr (!kGather)
         TW::fetch_q(next_q, q + ((int64_t)(s + 1) * hq + (int64_t)kh * G) * D);
     }
-    // Tile j + 1 goes into the other buffer once the wave has waited for
-    // everything: one tile in flight per wave while it computes.  Issuing it
-    // before the wait (two in flight while the wave waits; possible for the
-    // tile waves whose loads the compiler counts exactly) took 3% off 4,096
-    // short sequences but cost the bandwidth-bound batches 1.5-2.5%: more
-    // scattered requests outstanding per CU than the memory system serves
-    // well.  Done only on short segments, it left the compiler copies of
-    // undefined loop values that made it wait for all loads anyway.
+    // Tile j + 1 goes into the other buffer.  Two workgroups per CU: the
+    // wave waits for everything, then issues it, so one tile is in flight
+    // per wave while it computes.  kDeep (one workgroup per CU): tile j + 1
+    // is issued before the wait for tile j, so two are in flight while the
+    // wave waits, and the wait leaves tile j + 1's loads outstanding.  Eight
+    // waves per CU with two tiles each were 1.5-2.5% slower on the
+    // bandwidth-bound batches than with one (more scattered requests
+    // outstanding than the memory system serves well); four waves with two
+    // tiles each are 1.5-2% faster than eight with one.
     auto next = [&](uint4 (&kn)[KL], int buf, int jn) {
-      wait_vmem_all();
-      if (jn < ntiles) issue(kn, buf, jn);
+      if constexpr (kDeep) {
+        if (jn < ntiles) {
+          issue(kn, buf, jn);
+          wait_vmem_but<TW::kLoadsPerTile>();
+        } else {
+          wait_vmem_all();
+        }
+      } else {
+        wait_vmem_all();
+        if (jn < ntiles) issue(kn, buf, jn);
+      }
     };
     // Tiles in pairs, the loop's only exit at its top: a loop left from its
     // middle gave the compiler undefined loop values to copy, and the copy
@@ -632,13 +655,15 @@ static hipError_t launch_prefix_merge_d(const PrefixArgs& a) {
 
 // ---------------------------------------------------------------------------
 
-// Waves of one decode launch on the current device: kWorkgroupsPerCu
-// workgroups per CU, or fewer if fewer fit; kErrDoesNotFit if not one
-// workgroup fits a CU or its LDS exceeds the device's per-workgroup limit
-// (cached per instantiation and device; recomputing gives the same answer,
-// so concurrent first calls are harmless).
-template <typename T, typename KV, int D, int BS, int G>
+// Waves of one decode launch on the current device: `per_cu_max`
+// workgroups per CU (kWorkgroupsPerCu, or 1 for kDeep), or fewer if fewer
+// fit; kErrDoesNotFit if not one workgroup fits a CU or its LDS exceeds the
+// device's per-workgroup limit (cached per instantiation and device;
+// recomputing gives the same answer, so concurrent first calls are
+// harmless).
+template <typename T, typename KV, int D, int BS, int G, bool kDeep = false>
 static hipError_t launch_waves(int* waves) {
+  constexpr int per_cu_max = kDeep ? 1 : kWorkgroupsPerCu;
   static int cache[kMaxDevices];  // > 0 waves, -1 does not fit, 0 unknown
   static int lds_cache[kMaxDevices];
   int dev = 0;
@@ -650,7 +675,7 @@ static hipError_t launch_waves(int* waves) {
     *waves = cached;
     return cached > 0 ? hipSuccess : kErrDoesNotFit;
   }
-  auto kernel = pa_decode_streamk<T, D, BS, G, false, KV>;
+  auto kernel = pa_decode_streamk<T, D, BS, G, false, KV, kDeep>;
   e = check_lds((const void*)kernel, 0, lds_cache);
   if (e != hipSuccess && e != kErrDoesNotFit) return e;
   int cus = 0, per_cu = 0;
@@ -660,17 +685,17 @@ static hipError_t launch_waves(int* waves) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
     if (e != hipSuccess) return e;
   }
-  const int n = (per_cu > 0 && cus > 0) ? cus * min(per_cu, kWorkgroupsPerCu) * kWaves : -1;
+  const int n = (per_cu > 0 && cus > 0) ? cus * min(per_cu, per_cu_max) * kWaves : -1;
   __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
   *waves = n;
   return n > 0 ? hipSuccess : kErrDoesNotFit;
 }
 
-template <typename T, typename KV, int D, int BS, int G>
-static hipError_t launch_t(const StreamKArgs& a, bool gather) {
+template <typename T, typename KV, int D, int BS, int G, bool kDeep>
+static hipError_t launch_k(const StreamKArgs& a, bool gather) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
   int waves = 0;
-  hipError_t e = launch_waves<T, KV, D, BS, G>(&waves);
+  hipError_t e = launch_waves<T, KV, D, BS, G, kDeep>(&waves);
   if (e != hipSuccess) return e;
   // no more waves than the workspace holds partial slots for, a whole
   // number per KV head, at least one
@@ -680,7 +705,7 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   if constexpr (!std::is_same<KV, Vec>::value) {  // the gather probe reads as the matrix-core wave
     if (gather) {  // the same grid, gather-only (the group does not change the loads)
       static int lds_cache[kMaxDevices];
-      auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV>;
+      auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV, kDeep>;
       e = check_lds((const void*)kernel, 0, lds_cache);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kernel, dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
@@ -694,7 +719,7 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   } else {
     if (gather) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV>),
+  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV, kDeep>),
                      dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
                      (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
@@ -714,6 +739,30 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
                        a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta, a.seq_lens,
                        (int32_t)pairs, a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
   return hipGetLastError();
+}
+
+// kDeep (one workgroup per CU, two tiles in flight per wave) for the 16-bit
+// matrix-core tile wave on batches of few, long sequences, where every
+// wave's run is long and the launch is bound by the gather: at most
+// kDeepMaxPairs (sequence, KV head) pairs and tables of at least
+// kDeepMinLen positions.  Measured: the 256-sequence mixed step 344.5 ->
+// 339.4 us, the 32-sequence long context 391.6 -> 384.0 us.  Many short
+// sequences keep two workgroups per CU: with half the waves, 4,096
+// sequences of 16-64 positions took 245 instead of 225 us and 8,192 of 1-8
+// positions 339 instead of 258 us.  The shared-prefix tails (start > 0) are
+// short too.
+constexpr int64_t kDeepMaxPairs = 4096;
+constexpr int64_t kDeepMinLen = 1024;
+
+template <typename T, typename KV, int D, int BS, int G>
+static hipError_t launch_t(const StreamKArgs& a, bool gather) {
+  if constexpr (std::is_same<KV, T>::value) {
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t max_len = (int64_t)a.max_blocks_per_seq * a.block_size;
+    if (a.start == 0 && pairs <= kDeepMaxPairs && max_len >= kDeepMinLen)
+      return launch_k<T, KV, D, BS, G, true>(a, gather);
+  }
+  return launch_k<T, KV, D, BS, G, false>(a, gather);
 }
 
 template <typename T, typename KV, int D, int BS>

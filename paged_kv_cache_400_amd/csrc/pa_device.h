@@ -72,8 +72,27 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
-// Cache-policy operand of global_load_lds for the same hint (the nt bit).
+// Cache-policy operand of the copies into LDS (global_load_lds, buffer_load
+// ... lds) for the same hint (the nt bit).
 constexpr int kCachePolicyStream = 2;
+
+// A buffer resource for `bytes` bytes at p (raw: no stride, no format; a
+// load past the range reads 0; the last word is the gfx9 resource format).
+// Copies into LDS issued as buffer loads (buffer_load_dwordx4 ... lds) are
+// counted by the compiler among the wave's vector-memory operations like any
+// load.  A pending global_load_lds instead makes it wait for every
+// outstanding load (vmcnt(0)) before any use of a register another load
+// filled, which a driver that keeps several tiles in flight cannot afford.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from the resource at byte voffset into LDS at lds +
+// 16 * lane (the copy's destination is per instruction, not per lane).
+__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                              void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, kCachePolicyStream);
+}
 
 // ---- 2^x on the transcendental unit (v_exp_f32; 2^-inf = 0) -------------
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -132,6 +132,14 @@ __device__ __forceinline__ void stage_mfma_result(float* st, const f32x4_t (&acc
   }
 }
 
+// One 32-bit LDS read at byte address a, completed before the asm ends (for
+// the reason given at read_v_tr).
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+
 // The NM transpose reads of a V tile for one lane (column block m at byte
 // offset 32 m from the lane's LDS address a), as one asm block that waits for
 // its own results before it ends.  Written as builtins, these reads would
@@ -280,6 +288,37 @@ struct TileWave {
   __device__ __forceinline__ void issue_ids(uint4 (&kr)[KC], int buf, int t0, int t_last,
                                             const int (&ids)[kIds]) {
     issue(kr, buf, t0, t_last, ids[0], ids[kIds - 1]);
+  }
+
+  // issue_ids with the V copies as buffer loads: every load of the tile is
+  // then one the compiler counts, so a driver may keep the next tile in
+  // flight and wait for this one with wait_vmem_but<kLoadsPerTile>.  The
+  // rows of one copy lie in one block (for 8-position blocks, rows 8..15 in
+  // the second one unless all of them clamp back into the first).
+  static constexpr int kLoadsPerTile = KL + 4;
+  __device__ __forceinline__ void issue_ids_counted(uint4 (&kr)[KC], int buf, int t0, int t_last,
+                                                    const int (&ids)[kIds]) {
+    const int id0 = ids[0], id1 = ids[kIds - 1];
+    {
+      const uint16_t* kb0 = kc + (int64_t)id0 * blk_stride + head_off;
+      const uint16_t* kb1 = kc + (int64_t)id1 * blk_stride + head_off;
+      const int t = min(t0 + col, t_last);
+      const uint16_t* ptr = ((BS < kTile && t - t0 >= BS) ? kb1 : kb0) + (t % BS) * D + grp * 8;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kr[c] = load_stream(ptr + c * 32);
+    }
+    unsigned char* vt = vtile + buf * GE::TILE;
+    const __amdgpu_buffer_rsrc_t r0 = buffer_rsrc(vc + (int64_t)id0 * blk_stride + head_off,
+                                                  BS * D * 2);
+    const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(vc + (int64_t)id1 * blk_stride + head_off,
+                                                  BS * D * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(t0 + 4 * i + lane / (D / 8), t_last);
+      const bool second = BS < kTile && 4 * i >= BS && t0 + BS <= t_last;
+      const uint32_t off = (uint32_t)(((t % BS) * D + (lane % (D / 8)) * 8) * 2);
+      if (GE::LANES == 64 || lane < GE::LANES) copy_to_lds16(second ? r1 : r0, off, vt + i * GE::REGION);
+    }
   }
 
   // Compute the tile at t0 (positions >= t_end masked) whose K is in kr and
