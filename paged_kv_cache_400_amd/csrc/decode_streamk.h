@@ -314,6 +314,10 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   int next_L = 0, next_raw = 0;
   bool have_next = false, use_next = false;
   typename TW::QRegs next_q{};
+  // The vector tile wave at group 8 holds 8 heads' q, scores and sums per
+  // lane; the prefetch's registers (32 for q alone) made it spill 320 bytes
+  // per lane, so it reads the next sequence when its segment starts.
+  constexpr bool kPrefetch = !(std::is_same<KV, Vec>::value && G >= 8);
 
   int64_t g = g0;
   while (true) {
@@ -327,7 +331,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 
     tw.init(kc, vc, hkv, kh, vtile);
     if constexpr (!kGather) {
-      if (use_next)
+      if (kPrefetch && use_next)
         tw.qr = next_q;
       else
         tw.load_q(q + row0 * D);
@@ -393,7 +397,8 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
 
     uint4 ka[KL], kb[KL];
     issue(ka, 0, 0);
-    have_next = g + ntiles < g1 && s + 1 < num_seqs;  // the run goes on past this sequence
+    // the run goes on past this sequence
+    have_next = kPrefetch && g + ntiles < g1 && s + 1 < num_seqs;
     if (have_next) {
       next_L = seq_lens[s + 1];
       const int b0 = start / BS;  // the next segment's first block
@@ -426,16 +431,31 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
     // Tiles in pairs, the loop's only exit at its top: a loop left from its
     // middle gave the compiler undefined loop values to copy, and the copy
     // of an undefined register made it wait for every outstanding load.
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-      next(kb, 1, j + 1);
-      consume(ka, 0, p_lo + j * kT);
-      next(ka, 0, j + 2);
-      consume(kb, 1, p_lo + (j + 1) * kT);
-    }
-    if (j < ntiles) {
-      next(kb, 1, j + 1);
-      consume(ka, 0, p_lo + j * kT);
+    if constexpr (std::is_same<KV, Vec>::value) {
+      // the vector tile wave waits for everything before each issue, so a
+      // loop left from its middle costs it nothing, and its two copies of
+      // the tile step (not three) leave it fewer registers to spill at
+      // group 8
+      for (int j = 0;;) {
+        next(kb, 1, j + 1);
+        consume(ka, 0, p_lo + j * kT);
+        if (++j >= ntiles) break;
+        next(ka, 0, j + 1);
+        consume(kb, 1, p_lo + j * kT);
+        if (++j >= ntiles) break;
+      }
+    } else {
+      int j = 0;
+      for (; j + 1 < ntiles; j += 2) {
+        next(kb, 1, j + 1);
+        consume(ka, 0, p_lo + j * kT);
+        next(ka, 0, j + 2);
+        consume(kb, 1, p_lo + (j + 1) * kT);
+      }
+      if (j < ntiles) {
+        next(kb, 1, j + 1);
+        consume(ka, 0, p_lo + j * kT);
+      }
     }
     if constexpr (kGather) {
       if (gathered == 0x9e3779b9u && lane == 0) out[0] = (uint16_t)gathered;
