@@ -49,7 +49,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 
-@dataclass
+@dataclass(eq=False)  # compared by identity: the running list removes by object
 class Request:
     rid: int
     arrival: int          # first iteration at which it may be admitted
@@ -111,8 +111,16 @@ class Scheduler:
         return -(-tokens // self.bs)
 
     def blocks_used(self) -> int:
-        """Paged: blocks the running requests hold now."""
-        return sum(self.blocks(r.kv_tokens()) for r in self.running)
+        """Paged: blocks the running requests hold now (Request.kv_tokens
+        and blocks() written out: this runs over the running set twice an
+        iteration)."""
+        bs = self.bs
+        n = 0
+        for r in self.running:
+            p = r.prefilled
+            t = p + (r.generated - 1 if r.generated > 0 else 0) if p == r.prompt_len else p
+            n += -(-t // bs)
+        return n
 
     # ---- one iteration
     def step(self) -> StepPlan:
@@ -127,11 +135,13 @@ class Scheduler:
                 self._preempt(self.running[-1], plan)
                 self._plan(plan)
         # apply
-        pre = {rid: (first, k) for rid, first, k in plan.prefill}
+        pre = {rid: k for rid, _, k in plan.prefill}
+        dec = set(plan.decode)
         for r in self.running:
-            if r.rid in pre:
-                r.prefilled += pre[r.rid][1]
-            if r.rid in plan.decode:
+            k = pre.get(r.rid)
+            if k is not None:
+                r.prefilled += k
+            if r.rid in dec:
                 r.generated += 1
         for r in list(self.running):
             if r.generated >= r.gen_len and r.finished is None:
@@ -190,12 +200,18 @@ class Scheduler:
                 plan.padded.append(r.rid)  # static: its row still runs, to no use
 
     def _need(self, plan: StepPlan) -> int:
-        """Paged: blocks the running requests hold after this iteration."""
+        """Paged: blocks the running requests hold after this iteration
+        (Request.kv_tokens and blocks() written out)."""
         pre = {rid: k for rid, _, k in plan.prefill}
         dec = set(plan.decode)
-        return sum(self.blocks(r.kv_tokens(r.prefilled + pre.get(r.rid, 0),
-                                           r.generated + (1 if r.rid in dec else 0)))
-                   for r in self.running)
+        bs = self.bs
+        n = 0
+        for r in self.running:
+            p = r.prefilled + pre.get(r.rid, 0)
+            g = r.generated + (1 if r.rid in dec else 0)
+            t = p + (g - 1 if g > 0 else 0) if p == r.prompt_len else p
+            n += -(-t // bs)
+        return n
 
     def _preempt(self, r: Request, plan: StepPlan):
         self.running.remove(r)
@@ -294,30 +310,39 @@ class Executor:
         self.events = []
         return t
 
-    def row_of(self, rid: int, pos):
-        return (np.int64(rid) * 7919 + np.asarray(pos, dtype=np.int64) * 104729) % self.rows
+    def row_of(self, rid, pos):
+        """Table row of (request, position); either may be an array."""
+        return (np.asarray(rid, dtype=np.int64) * 7919 +
+                np.asarray(pos, dtype=np.int64) * 104729) % self.rows
 
-    def token_of(self, rid: int, pos):
-        return ((np.int64(rid) << 16) ^ np.asarray(pos, dtype=np.int64)) & 0x3FFFFFFF
+    def token_of(self, rid, pos):
+        return ((np.asarray(rid, dtype=np.int64) << 16) ^
+                np.asarray(pos, dtype=np.int64)) & 0x3FFFFFFF
 
-    def _write(self, rids_pos, slots):
-        """Append the rows of (rid, position) pairs at the given slots."""
-        torch = self.torch
-        idx = np.concatenate([self.row_of(r, p) for r, p in rids_pos]) if rids_pos else []
-        if len(idx) == 0:
+    def _upload(self, a):
+        """A host array on the device without waiting for the GPU: staged in
+        pinned memory from torch's caching host allocator (which keeps the
+        staging buffer until the copy has run) and copied asynchronously on
+        the current stream, so the host can plan the next iteration while
+        the kernels run."""
+        t = self.torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+        return t.to(self.device, non_blocking=True)
+
+    def _write(self, rows, slots):
+        """Append the key and value rows `rows` of the table at `slots`."""
+        if len(rows) == 0:
             return
-        ix = torch.from_numpy(np.asarray(idx, np.int64)).to(self.device)
+        ix = self._upload(np.asarray(rows, np.int64))
         kv = self.kv_dev.index_select(0, ix)
-        sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to(self.device)
+        sl = self._upload(np.asarray(slots, dtype=np.int32))
         k, v = kv[:, 0].contiguous(), kv[:, 1].contiguous()
         self._timed(self.pa.reshape_and_cache, k, v, self.k_cache, self.v_cache, sl)
         return kv, sl
 
     def _tables(self, rids):
-        mb = max(1, max(-(-self.kv_len[r] // self.bs) for r in rids))
+        mb = max(1, -(-max(self.kv_len[r] for r in rids) // self.bs))
         t, lens = self.bm.tables(rids, mb)
-        dev = self.device
-        return (self.torch.from_numpy(t).to(dev), self.torch.from_numpy(lens).to(dev), t, lens)
+        return self._upload(t), self._upload(lens), t, lens
 
     def iteration(self, sched: Scheduler, observe=None):
         """One scheduler step and the kernels it calls; returns the plan."""
@@ -331,7 +356,7 @@ class Executor:
                 del self.kv_len[rid]
         # prompt chunks: place, write, attend
         if plan.prefill:
-            written, slots, q_rows, qs, prids = [], [], [], [0], []
+            slots, q_rows, qs, prids = [], [], [0], []
             for rid, first, k in plan.prefill:
                 pos = np.arange(first, first + k)
                 toks = self.token_of(rid, pos).astype(np.int32)
@@ -340,16 +365,15 @@ class Executor:
                 else:
                     sl, _ = self.bm.append(rid, toks)
                 self.kv_len[rid] = first + k
-                written.append((rid, pos))
                 slots.append(sl)
                 q_rows.append(self.row_of(rid, pos))
                 qs.append(qs[-1] + k)
                 prids.append(rid)
-            kv, sl = self._write(written, np.concatenate(slots))
-            q = self.q_dev.index_select(
-                0, torch.from_numpy(np.concatenate(q_rows)).to(self.device))
+            rows = np.concatenate(q_rows)  # a token's q, key and value share its row
+            kv, sl = self._write(rows, np.concatenate(slots))
+            q = self.q_dev.index_select(0, self._upload(rows))
             bt, lens, bt_h, lens_h = self._tables(prids)
-            qs_d = torch.from_numpy(np.asarray(qs, np.int32)).to(self.device)
+            qs_d = self._upload(np.asarray(qs, np.int32))
             out = self._timed(self.pa.prefill, q, self.k_cache, self.v_cache, bt, lens, qs_d,
                               scale=self.scale)
             info["prefill"] = (prids, q, qs, bt_h, lens_h, out)
@@ -358,18 +382,17 @@ class Executor:
                      if first + k == by_id[rid].prompt_len}
         drids = [rid for rid in plan.decode if rid not in completes]
         if drids:
-            pos = [self.kv_len[r] for r in drids]
-            toks = np.array([self.token_of(r, p) for r, p in zip(drids, pos)], np.int32)
-            sl, cow = self.bm.append_batch(np.asarray(drids, np.int64), toks)
+            rid_a = np.asarray(drids, np.int64)
+            pos = np.fromiter((self.kv_len[r] for r in drids), np.int64, len(drids))
+            sl, cow = self.bm.append_batch(rid_a, self.token_of(rid_a, pos).astype(np.int32))
             assert len(cow) == 0
             for r in drids:
                 self.kv_len[r] += 1
-            self._write([(r, [p]) for r, p in zip(drids, pos)], sl)
+            self._write(self.row_of(rid_a, pos), sl)
         rows = drids + [rid for rid in plan.padded if rid in self.kv_len]
         if rows:
-            q = self.q_dev.index_select(0, torch.from_numpy(
-                np.array([self.row_of(r, self.kv_len[r] - 1) for r in rows], np.int64)
-            ).to(self.device))
+            last = np.fromiter((self.kv_len[r] - 1 for r in rows), np.int64, len(rows))
+            q = self.q_dev.index_select(0, self._upload(self.row_of(rows, last)))
             bt, lens, bt_h, lens_h = self._tables(rows)
             need = self.pa.decode_workspace_bytes(len(rows), self.hq, self.d, bt.shape[1], self.bs)
             if self.ws is None or self.ws.numel() < need:

@@ -44,6 +44,22 @@ def test_many_short_sequences(part):
     compare(out, oracle_out(b, kp, vp), label=f"many_short part{part}", round_slack=True)
 
 
+@pytest.mark.parametrize("impl", ["auto", "mfma", "valu"])
+def test_runs_across_many_sequences_group8(impl):
+    """Group 8 with each tile wave: short sequences (empty ones among them)
+    and a few long ones, so the balanced split's runs cross many sequence
+    boundaries.  The vector tile wave at group 8 reads each next sequence
+    when its segment starts (no prefetch); the matrix-core wave prefetches
+    it, in the deep mode or not."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 40, 400).tolist()
+    lens[50], lens[200], lens[333] = 2500, 0, 1800
+    b = wl.make_decode_batch("runs_g8", lens, 64, 8, 128, 16, "bf16", seed=32, append=1)
+    out, dev = gpu_step(b, impl=impl)
+    kp, vp = oracle_pools(b)
+    compare(out, oracle_out(b, kp, vp), label=f"runs g8 {impl}", round_slack=True)
+
+
 @pytest.mark.parametrize("part", SPLITS)
 @pytest.mark.parametrize("bs", [8, 32])
 def test_one_long_sequence_one_kv_head(part, bs):
