@@ -115,8 +115,9 @@ typedef enum pa_dtype {
  * (how a run's tiles are computed) is chosen by the query group: at group 1
  * the vector unit alone (as pa_decode_valu), from group 2 on the matrix
  * cores (q.K^T and P.V as MFMA, the G query heads on the MFMA's N axis).
- * Measured on the 256-sequence mixed step at groups 1/2/4/8, the matrix
- * cores take the same time at group 1 and save 1%, 7% and 46% above it.
+ * Measured on the 256-sequence mixed step at groups 1/2/4/8: at group 1
+ * the vector unit is 1% faster; above it the vector unit takes 2%, 8% and
+ * 51% longer than the matrix cores.
  * The workspace needs
  * pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents on
  * entry do not matter and on return are unspecified.
