@@ -122,9 +122,10 @@ struct TileWaveOf<T, Vec, D, BS, G> {
 // 8-bit tile wave uses 190 of them (with the 168 that three waves allow it
 // spent 8% more time on the mixed step), the 16-bit one about 150.
 //
-// kDeep: one workgroup per CU instead of two, each wave with two tiles in
-// flight instead of one (the 16-bit matrix-core tile wave only, whose loads
-// the compiler counts exactly; see the walk below).
+// kDeep: each wave with two tiles in flight instead of one (the 16-bit
+// matrix-core tile wave only, whose loads the compiler counts exactly; see
+// the walk below).  The launch puts one workgroup of these on each CU for
+// batches of few long sequences, two for the rest (launch_t).
 template <typename T, int D, int BS, int G, bool kGather, typename KV, bool kDeep = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
@@ -406,15 +407,16 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       if constexpr (!kGather)
         TW::fetch_q(next_q, q + ((int64_t)(s + 1) * hq + (int64_t)kh * G) * D);
     }
-    // Tile j + 1 goes into the other buffer.  Two workgroups per CU: the
-    // wave waits for everything, then issues it, so one tile is in flight
-    // per wave while it computes.  kDeep (one workgroup per CU): tile j + 1
-    // is issued before the wait for tile j, so two are in flight while the
-    // wave waits, and the wait leaves tile j + 1's loads outstanding.  Eight
-    // waves per CU with two tiles each were 1.5-2.5% slower on the
-    // bandwidth-bound batches than with one (more scattered requests
-    // outstanding than the memory system serves well); four waves with two
-    // tiles each are 1.5-2% faster than eight with one.
+    // Tile j + 1 goes into the other buffer.  Without kDeep the wave waits
+    // for everything, then issues it, so one tile is in flight per wave
+    // while it computes.  kDeep: tile j + 1 is issued before the wait for
+    // tile j, so two are in flight while the wave waits, and the wait leaves
+    // tile j + 1's loads outstanding.  On the bandwidth-bound batches, eight
+    // waves per CU with two tiles each were 1.5-2.5% slower than with one
+    // (more scattered requests outstanding than the memory system serves
+    // well), and four waves with two tiles each 1.5-2% faster than eight
+    // with one; on many short sequences eight waves with two tiles each are
+    // the fastest.
     auto next = [&](uint4 (&kn)[KL], int buf, int jn) {
       if constexpr (kDeep) {
         if (jn < ntiles) {
@@ -675,22 +677,22 @@ static hipError_t launch_prefix_merge_d(const PrefixArgs& a) {
 
 // ---------------------------------------------------------------------------
 
-// Waves of one decode launch on the current device: `per_cu_max`
-// workgroups per CU (kWorkgroupsPerCu, or 1 for kDeep), or fewer if fewer
-// fit; kErrDoesNotFit if not one workgroup fits a CU or its LDS exceeds the
-// device's per-workgroup limit (cached per instantiation and device;
-// recomputing gives the same answer, so concurrent first calls are
-// harmless).
+// Waves of one decode launch on the current device: per_cu_max (1 or
+// kWorkgroupsPerCu) workgroups per CU, or fewer if fewer fit;
+// kErrDoesNotFit if not one workgroup fits a CU or its LDS exceeds the
+// device's per-workgroup limit (cached per instantiation, device and
+// per_cu_max; recomputing gives the same answer, so concurrent first calls
+// are harmless).
 template <typename T, typename KV, int D, int BS, int G, bool kDeep = false>
-static hipError_t launch_waves(int* waves) {
-  constexpr int per_cu_max = kDeep ? 1 : kWorkgroupsPerCu;
-  static int cache[kMaxDevices];  // > 0 waves, -1 does not fit, 0 unknown
+static hipError_t launch_waves(int* waves, int per_cu_max) {
+  if (per_cu_max < 1 || per_cu_max > kWorkgroupsPerCu) return hipErrorInvalidValue;
+  static int cache[kMaxDevices][kWorkgroupsPerCu + 1];  // > 0 waves, -1 does not fit, 0 unknown
   static int lds_cache[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  const int cached = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  const int cached = __atomic_load_n(&cache[dev][per_cu_max], __ATOMIC_RELAXED);
   if (cached != 0) {
     *waves = cached;
     return cached > 0 ? hipSuccess : kErrDoesNotFit;
@@ -706,16 +708,16 @@ static hipError_t launch_waves(int* waves) {
     if (e != hipSuccess) return e;
   }
   const int n = (per_cu > 0 && cus > 0) ? cus * min(per_cu, per_cu_max) * kWaves : -1;
-  __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  __atomic_store_n(&cache[dev][per_cu_max], n, __ATOMIC_RELAXED);
   *waves = n;
   return n > 0 ? hipSuccess : kErrDoesNotFit;
 }
 
 template <typename T, typename KV, int D, int BS, int G, bool kDeep>
-static hipError_t launch_k(const StreamKArgs& a, bool gather) {
+static hipError_t launch_k(const StreamKArgs& a, bool gather, int per_cu_max) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
   int waves = 0;
-  hipError_t e = launch_waves<T, KV, D, BS, G, kDeep>(&waves);
+  hipError_t e = launch_waves<T, KV, D, BS, G, kDeep>(&waves, per_cu_max);
   if (e != hipSuccess) return e;
   // no more waves than the workspace holds partial slots for, a whole
   // number per KV head, at least one
@@ -761,16 +763,18 @@ static hipError_t launch_k(const StreamKArgs& a, bool gather) {
   return hipGetLastError();
 }
 
-// kDeep (one workgroup per CU, two tiles in flight per wave) for the 16-bit
-// matrix-core tile wave on batches of few, long sequences, where every
-// wave's run is long and the launch is bound by the gather: at most
-// kDeepMaxPairs (sequence, KV head) pairs and tables of at least
-// kDeepMinLen positions.  Measured: the 256-sequence mixed step 344.5 ->
-// 339.4 us, the 32-sequence long context 391.6 -> 384.0 us.  Many short
-// sequences keep two workgroups per CU: with half the waves, 4,096
-// sequences of 16-64 positions took 245 instead of 225 us and 8,192 of 1-8
-// positions 339 instead of 258 us.  The shared-prefix tails (start > 0) are
-// short too.
+// The 16-bit matrix-core tile wave always keeps two tiles in flight
+// (kDeep).  On batches of few, long sequences, where every wave's run is
+// long and the launch is bound by the gather (at most kDeepMaxPairs
+// (sequence, KV head) pairs, tables of at least kDeepMinLen positions), the
+// launch puts one workgroup on each CU; measured against two workgroups of
+// one tile in flight each: the 256-sequence mixed step 344.5 -> 339.4 us,
+// the 32-sequence long context 391.6 -> 384.0 us.  Other batches get two
+// workgroups per CU: with one, 4,096 sequences of 16-64 positions took 245
+// us and 8,192 of 1-8 positions 339 us, against 220 and 256 us with two
+// (225 and 258 us with two of one tile in flight each).  The shared-prefix
+// tails (start > 0) are short too.  The 8-bit and vector tile waves keep
+// one tile in flight, two workgroups per CU.
 constexpr int64_t kDeepMaxPairs = 4096;
 constexpr int64_t kDeepMinLen = 1024;
 
@@ -779,10 +783,10 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   if constexpr (std::is_same<KV, T>::value) {
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t max_len = (int64_t)a.max_blocks_per_seq * a.block_size;
-    if (a.start == 0 && pairs <= kDeepMaxPairs && max_len >= kDeepMinLen)
-      return launch_k<T, KV, D, BS, G, true>(a, gather);
+    const bool few_long = a.start == 0 && pairs <= kDeepMaxPairs && max_len >= kDeepMinLen;
+    return launch_k<T, KV, D, BS, G, true>(a, gather, few_long ? 1 : kWorkgroupsPerCu);
   }
-  return launch_k<T, KV, D, BS, G, false>(a, gather);
+  return launch_k<T, KV, D, BS, G, false>(a, gather, kWorkgroupsPerCu);
 }
 
 template <typename T, typename KV, int D, int BS>
