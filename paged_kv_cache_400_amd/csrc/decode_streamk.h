@@ -118,9 +118,10 @@ struct TileWaveOf<T, Vec, D, BS, G> {
 // a value it cannot be expected to hit).  KV is the pool element type (T, or
 // FP8 with out_scale = v_scale applied to every result; for 16-bit pools
 // out_scale is not used).  Two waves per SIMD are all the launch uses
-// (kWorkgroupsPerCu), so the compiler may take up to 256 registers; the
-// 8-bit tile wave uses 190 of them (with the 168 that three waves allow it
-// spent 8% more time on the mixed step), the 16-bit one about 150.
+// (kWorkgroupsPerCu), so the compiler may take up to 256 registers; at
+// d 128 the 8-bit tile wave uses 219 of them (with the 168 that three waves
+// allow it spent 8% more time on the mixed step), the vector-unit one up to
+// 222 and the 16-bit matrix-core one 175.
 //
 // kDeep: each wave with two tiles in flight instead of one (the 16-bit
 // matrix-core tile wave only, whose loads the compiler counts exactly; see
@@ -785,8 +786,9 @@ static hipError_t launch_t(const StreamKArgs& a, bool gather) {
     const int64_t max_len = (int64_t)a.max_blocks_per_seq * a.block_size;
     const bool few_long = a.start == 0 && pairs <= kDeepMaxPairs && max_len >= kDeepMinLen;
     return launch_k<T, KV, D, BS, G, true>(a, gather, few_long ? 1 : kWorkgroupsPerCu);
+  } else {
+    return launch_k<T, KV, D, BS, G, false>(a, gather, kWorkgroupsPerCu);
   }
-  return launch_k<T, KV, D, BS, G, false>(a, gather, kWorkgroupsPerCu);
 }
 
 template <typename T, typename KV, int D, int BS>
