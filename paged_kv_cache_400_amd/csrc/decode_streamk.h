@@ -12,8 +12,9 @@
 //
 // Tile order: for each KV head, the sequences' tiles back to back, sequence
 // s holding ceil(L_s / n) tiles of n positions (n = 16 for 16-bit pools, 32
-// for 8-bit ones).  The launch has two workgroups (8 waves) per CU, all
-// resident at once (a whole number of waves per KV head); wave w works on
+// for 8-bit ones).  The launch has two workgroups (8 waves) per CU, or one
+// on batches of few long sequences for the 16-bit matrix-core tile wave,
+// all resident at once (a whole number of waves per KV head); wave w works on
 // head w % hkv and takes the (w / hkv)-th of that head's equal runs of
 // units.  A unit is a tile, or with an explicit partition_size a partition
 // of that many positions (runs then start and end only at partition
@@ -42,10 +43,12 @@
 //     sum 2^(m_p - M) l_p) and writes the zero rows of empty sequences and
 //     the NaN rows of sequences whose length breaks the contract.
 // Within a pair a wave consumes its tiles in order with TileWave
-// (pa_mfma.h) or TileWave8 (pa_mfma_fp8.h): K to registers, V to LDS, q.K^T
-// and P.V on MFMA, each tile issued one tile ahead.  The run's block ids are
-// staged in a register, one per lane, and read with v_readlane: no memory
-// access between two tiles.
+// (pa_mfma.h) or TileWave8 (pa_mfma_fp8.h) -- K to registers, V to LDS,
+// q.K^T and P.V on MFMA -- or with TileWaveV (pa_valu.h, the vector unit
+// alone, K and V to registers).  Each tile is issued one tile ahead of its
+// use, two tiles ahead for the 16-bit matrix-core tile wave (kDeep).  The
+// run's block ids are staged in a register, one per lane, and read with
+// v_readlane: no memory access between two tiles.
 #pragma once
 
 #include <type_traits>
