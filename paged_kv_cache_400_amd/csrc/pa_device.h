@@ -73,8 +73,10 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 // Cache-policy operand of the copies into LDS (global_load_lds, buffer_load
-// ... lds) for the same hint (the nt bit).
+// ... lds) for the same hint (the nt bit), and the default policy for data
+// that other workgroups read again soon (prefill's K/V tiles).
 constexpr int kCachePolicyStream = 2;
+constexpr int kCachePolicyReuse = 0;
 
 // A buffer resource for `bytes` bytes at p (raw: no stride, no format; a
 // load past the range reads 0; the last word is the gfx9 resource format).
