@@ -130,7 +130,11 @@ struct TileWaveOf<T, Vec, D, BS, G> {
 // matrix-core tile wave only, whose loads the compiler counts exactly; see
 // the walk below).  The launch puts one workgroup of these on each CU for
 // batches of few long sequences, two for the rest (launch_t).
-template <typename T, int D, int BS, int G, bool kGather, typename KV, bool kDeep = false>
+//
+// kNt: the K/V loads carry the streaming hint (kDeep only may drop it; see
+// launch_t).
+template <typename T, int D, int BS, int G, bool kGather, typename KV, bool kDeep = false,
+          bool kNt = true>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
                   float2* __restrict__ ws_ml, int4* __restrict__ ws_meta,
@@ -146,6 +150,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
   constexpr int KL = TW::KL, kT = TW::kTileLen, kIds = TW::kIds;
   constexpr bool kScaled = std::is_same<KV, FP8>::value;
   static_assert(!kDeep || std::is_same<KV, T>::value, "kDeep: the 16-bit matrix-core tile wave");
+  static_assert(kNt || kDeep, "the K/V loads without the streaming hint: kDeep only");
   __shared__ __attribute__((aligned(16))) unsigned char s_mem[kWaves * 2 * TW::kTileBytes];
   static_assert(sizeof(s_mem) <= kMaxLdsBytes, "one workgroup's LDS fits gfx950's 160 KiB");
   static_assert(kWorkgroupsPerCu * sizeof(s_mem) <= kMaxLdsBytes,
@@ -395,7 +400,7 @@ pa_decode_streamk(uint16_t* __restrict__ out, float* __restrict__ ws_acc,
       for (int i = 1; i < kIds; ++i)
         ids[i] = (t0 + i * BS < p_end) ? __builtin_amdgcn_readlane(vid, b + i) : ids[0];
       if constexpr (kDeep)
-        tw.issue_ids_counted(kr, buf, t0, p_end - 1, ids);
+        tw.template issue_ids_counted<kNt>(kr, buf, t0, p_end - 1, ids);
       else
         tw.issue_ids(kr, buf, t0, p_end - 1, ids);
     };
@@ -687,7 +692,7 @@ static hipError_t launch_prefix_merge_d(const PrefixArgs& a) {
 // device's per-workgroup limit (cached per instantiation, device and
 // per_cu_max; recomputing gives the same answer, so concurrent first calls
 // are harmless).
-template <typename T, typename KV, int D, int BS, int G, bool kDeep = false>
+template <typename T, typename KV, int D, int BS, int G, bool kDeep = false, bool kNt = true>
 static hipError_t launch_waves(int* waves, int per_cu_max) {
   if (per_cu_max < 1 || per_cu_max > kWorkgroupsPerCu) return hipErrorInvalidValue;
   static int cache[kMaxDevices][kWorkgroupsPerCu + 1];  // > 0 waves, -1 does not fit, 0 unknown
@@ -701,7 +706,7 @@ static hipError_t launch_waves(int* waves, int per_cu_max) {
     *waves = cached;
     return cached > 0 ? hipSuccess : kErrDoesNotFit;
   }
-  auto kernel = pa_decode_streamk<T, D, BS, G, false, KV, kDeep>;
+  auto kernel = pa_decode_streamk<T, D, BS, G, false, KV, kDeep, kNt>;
   e = check_lds((const void*)kernel, 0, lds_cache);
   if (e != hipSuccess && e != kErrDoesNotFit) return e;
   int cus = 0, per_cu = 0;
@@ -717,11 +722,11 @@ static hipError_t launch_waves(int* waves, int per_cu_max) {
   return n > 0 ? hipSuccess : kErrDoesNotFit;
 }
 
-template <typename T, typename KV, int D, int BS, int G, bool kDeep>
+template <typename T, typename KV, int D, int BS, int G, bool kDeep, bool kNt = true>
 static hipError_t launch_k(const StreamKArgs& a, bool gather, int per_cu_max) {
   using Elem = typename TileWaveOf<T, KV, D, BS, G>::type::Elem;
   int waves = 0;
-  hipError_t e = launch_waves<T, KV, D, BS, G, kDeep>(&waves, per_cu_max);
+  hipError_t e = launch_waves<T, KV, D, BS, G, kDeep, kNt>(&waves, per_cu_max);
   if (e != hipSuccess) return e;
   // no more waves than the workspace holds partial slots for, a whole
   // number per KV head, at least one
@@ -731,7 +736,7 @@ static hipError_t launch_k(const StreamKArgs& a, bool gather, int per_cu_max) {
   if constexpr (!std::is_same<KV, Vec>::value) {  // the gather probe reads as the matrix-core wave
     if (gather) {  // the same grid, gather-only (the group does not change the loads)
       static int lds_cache[kMaxDevices];
-      auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV, kDeep>;
+      auto kernel = pa_decode_streamk<T, D, BS, 1, true, KV, kDeep, kNt>;
       e = check_lds((const void*)kernel, 0, lds_cache);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kernel, dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
@@ -745,7 +750,7 @@ static hipError_t launch_k(const StreamKArgs& a, bool gather, int per_cu_max) {
   } else {
     if (gather) return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV, kDeep>),
+  hipLaunchKernelGGL((pa_decode_streamk<T, D, BS, G, false, KV, kDeep, kNt>),
                      dim3((uint32_t)((waves + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, a.stream, (uint16_t*)a.out, a.ws_acc, a.ws_ml, a.ws_meta,
                      (const uint16_t*)a.q, (const Elem*)a.k_cache, (const Elem*)a.v_cache,
@@ -782,13 +787,29 @@ static hipError_t launch_k(const StreamKArgs& a, bool gather, int per_cu_max) {
 constexpr int64_t kDeepMaxPairs = 4096;
 constexpr int64_t kDeepMinLen = 1024;
 
+// The streaming hint lets the caches drop each K/V line once it is read:
+// right when the batch's K/V is far larger than the last-level cache (256
+// MiB on MI355X), as on the mixed step (without it 340 -> 384 us) and the
+// long context (384 -> 437 us).  When all the K/V a call can read fits in
+// that cache -- the smaller of the pool and the tables' capacity -- the
+// lines stay there across calls and across the sequences that share them:
+// without the hint the 64 sequences on one 2048-position prefix decode in
+// 64.6 instead of 82.5 us (their 81 MB of distinct K/V is read 7.5 times),
+// the pages' worked example (64 MB of tables) in 24.1 instead of 25.4 us.
+constexpr int64_t kCacheResidentBytes = int64_t(256) << 20;
+
 template <typename T, typename KV, int D, int BS, int G>
 static hipError_t launch_t(const StreamKArgs& a, bool gather) {
   if constexpr (std::is_same<KV, T>::value) {
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t max_len = (int64_t)a.max_blocks_per_seq * a.block_size;
     const bool few_long = a.start == 0 && pairs <= kDeepMaxPairs && max_len >= kDeepMinLen;
-    return launch_k<T, KV, D, BS, G, true>(a, gather, few_long ? 1 : kWorkgroupsPerCu);
+    const int per_cu = few_long ? 1 : kWorkgroupsPerCu;
+    const int64_t block_bytes = (int64_t)2 * a.num_kv_heads * BS * D * sizeof(uint16_t);  // K + V
+    const int64_t reach = min((int64_t)a.num_blocks, (int64_t)a.num_seqs * a.max_blocks_per_seq);
+    if (reach * block_bytes <= kCacheResidentBytes)
+      return launch_k<T, KV, D, BS, G, true, false>(a, gather, per_cu);
+    return launch_k<T, KV, D, BS, G, true, true>(a, gather, per_cu);
   } else {
     return launch_k<T, KV, D, BS, G, false>(a, gather, kWorkgroupsPerCu);
   }

@@ -72,6 +72,14 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
+// The same load without the hint when kNt is false.
+template <bool kNt>
+__device__ __forceinline__ uint4 load_kv(const void* p) {
+  if constexpr (kNt)
+    return load_stream(p);
+  else
+    return *reinterpret_cast<const uint4*>(p);
+}
 // Cache-policy operand of the copies into LDS (global_load_lds, buffer_load
 // ... lds) for the same hint (the nt bit), and the default policy for data
 // that other workgroups read again soon (prefill's K/V tiles).
@@ -90,10 +98,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
 }
 // 16 bytes per lane from the resource at byte voffset into LDS at lds +
 // 16 * lane (the copy's destination is per instruction, not per lane).
+template <int kPolicy = kCachePolicyStream>
 __device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
                                               void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voffset, 0, 0, kCachePolicyStream);
+                                           voffset, 0, 0, kPolicy);
 }
 
 // ---- 2^x on the transcendental unit (v_exp_f32; 2^-inf = 0) -------------

@@ -295,7 +295,11 @@ struct TileWave {
   // flight and wait for this one with wait_vmem_but<kLoadsPerTile>.  The
   // rows of one copy lie in one block (for 8-position blocks, rows 8..15 in
   // the second one unless all of them clamp back into the first).
+  // kNt: the streaming hint on every load (each byte read once, the batch's
+  // K/V far larger than the caches); without it, K/V that the last-level
+  // cache holds is read from there.
   static constexpr int kLoadsPerTile = KL + 4;
+  template <bool kNt = true>
   __device__ __forceinline__ void issue_ids_counted(uint4 (&kr)[KC], int buf, int t0, int t_last,
                                                     const int (&ids)[kIds]) {
     const int id0 = ids[0], id1 = ids[kIds - 1];
@@ -305,7 +309,7 @@ struct TileWave {
       const int t = min(t0 + col, t_last);
       const uint16_t* ptr = ((BS < kTile && t - t0 >= BS) ? kb1 : kb0) + (t % BS) * D + grp * 8;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kr[c] = load_stream(ptr + c * 32);
+      for (int c = 0; c < KC; ++c) kr[c] = load_kv<kNt>(ptr + c * 32);
     }
     unsigned char* vt = vtile + buf * GE::TILE;
     const __amdgpu_buffer_rsrc_t r0 = buffer_rsrc(vc + (int64_t)id0 * blk_stride + head_off,
@@ -317,7 +321,9 @@ struct TileWave {
       const int t = min(t0 + 4 * i + lane / (D / 8), t_last);
       const bool second = BS < kTile && 4 * i >= BS && t0 + BS <= t_last;
       const uint32_t off = (uint32_t)(((t % BS) * D + (lane % (D / 8)) * 8) * 2);
-      if (GE::LANES == 64 || lane < GE::LANES) copy_to_lds16(second ? r1 : r0, off, vt + i * GE::REGION);
+      if (GE::LANES == 64 || lane < GE::LANES)
+        copy_to_lds16<kNt ? kCachePolicyStream : kCachePolicyReuse>(second ? r1 : r0, off,
+                                                                     vt + i * GE::REGION);
     }
   }
 
