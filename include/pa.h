@@ -116,8 +116,8 @@ typedef enum pa_dtype {
  * the vector unit alone (as pa_decode_valu), from group 2 on the matrix
  * cores (q.K^T and P.V as MFMA, the G query heads on the MFMA's N axis).
  * Measured on the 256-sequence mixed step at groups 1/2/4/8: at group 1
- * the vector unit is 1% faster; above it the vector unit takes 2%, 8% and
- * 51% longer than the matrix cores.
+ * the vector unit is 1-2% faster; above it the vector unit takes 2%, 9% and
+ * 54% longer than the matrix cores.
  * The workspace needs
  * pa_decode_workspace_bytes(...) bytes (0: may be NULL); its contents on
  * entry do not matter and on return are unspecified.

@@ -126,8 +126,8 @@ namespace {
 
 // kAuto: pa_decode, the balanced split with the tile wave chosen by the
 // query group (the vector unit at group 1, the matrix cores above; measured
-// on the mixed step: at group 1 the vector unit is 1% faster, at groups 2, 4
-// and 8 it takes 2%, 8% and 51% longer).  kMfma: the matrix-core tile
+// on the mixed step: at group 1 the vector unit is 1-2% faster, at groups 2,
+// 4 and 8 it takes 2%, 9% and 54% longer).  kMfma: the matrix-core tile
 // wave at every group (pa_probe_decode_mfma).  kValu: pa_decode_valu.
 enum class Impl { kAuto, kMfma, kValu };
 
