@@ -16,6 +16,9 @@ and copy-on-write), and the batch a sequence decodes in changes every step
   * sharing: the shared-prefix step (one physical copy of the prefix,
     copy-on-write of the partial block) gives bit-identical outputs to the
     same sequences each holding a private copy of the prefix;
+  * the cache hint: the same batch in a pool that fits in the last-level
+    cache and in one that does not (read without and with the streaming
+    hint) decodes bit for bit alike;
   * batch composition: a sequence decoded alone, or inside a smaller batch,
     against the same sequence inside the 256-sequence mixed step.
     pa_decode_valu with a partition_size (here 512) is bitwise
@@ -33,7 +36,7 @@ import pytest
 import torch
 
 import paged_kv_cache_400_amd as pa
-from _gpu import compare, gpu_step, gpu_step_fp8, oracle_out
+from _gpu import compare, gpu_step, gpu_step_fp8, oracle_out, oracle_pools
 from paged_kv_cache_400_amd import workload as wl
 
 pytestmark = pytest.mark.gpu
@@ -95,6 +98,35 @@ def test_shared_prefix_equals_private_copies(part):
     assert torch.equal(o1.cpu().view(torch.int16), o2.cpu().view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_cache_hint_choice_is_bit_invariant(dtype):
+    """pa_decode reads K/V without the streaming hint when everything a call
+    can reach (the smaller of the pool and the tables' capacity) fits in 256
+    MiB, with it otherwise.  The hint changes only where lines are cached:
+    the same batch in its own pool and copied into a pool past 256 MiB (the
+    same block ids, the rest of the pool NaN) decodes bit for bit alike."""
+    lens = _lens(64, 600, 1100, 6)           # 64 x 70 table entries > 4,096 blocks
+    b = wl.make_decode_batch("hint", lens, 32, 8, 128, 16, dtype, seed=52, append=1)
+    block_bytes = 2 * 8 * 16 * 128 * 2        # K + V of one block, all heads
+    reach = min(b.num_blocks, len(lens) * b.max_blocks_per_seq)
+    assert reach * block_bytes <= 256 << 20 < len(lens) * b.max_blocks_per_seq * block_bytes
+    out_small, dev = gpu_step(b)               # the append, then the cache-resident decode
+    big_blocks = (256 << 20) // block_bytes + 200
+    assert big_blocks > b.num_blocks
+    big = {}
+    for name in ("k_cache", "v_cache"):
+        t = torch.full((big_blocks,) + tuple(dev[name].shape[1:]), float("nan"),
+                       dtype=dev[name].dtype, device=DEV)
+        t[:b.num_blocks] = dev[name]
+        big[name] = t
+    out_big = pa.decode(dev["q"], big["k_cache"], big["v_cache"], dev["block_tables"],
+                        dev["seq_lens"], scale=b.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_small.view(torch.int16), out_big.view(torch.int16))
+    kp, vp = oracle_pools(b)
+    compare(out_small, oracle_out(b, kp, vp), label=f"cache hint {dtype}")
+
+
 def _decode(dev, rows, impl, b, part=0):
     """pa_decode (or pa_decode_valu) of the sequences `rows` (a slice) as
     their own batch, over the full batch's pools."""
@@ -125,7 +157,6 @@ def test_batch_composition():
         assert diff <= 1e-2, (rows, diff)
     idx = np.arange(256)[slice(37, 38 + 90)]
     pairs = np.array([(s, h) for s in idx for h in range(b.num_q_heads)], np.int32)
-    from _gpu import oracle_pools
     kp, vp = oracle_pools(b)
     ref = oracle_out(b, kp, vp, pairs=pairs)
     got = _decode(dev, slice(37, 38 + 90), "auto", b)
