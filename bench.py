@@ -677,15 +677,16 @@ SERVE_WORKLOAD = ("serve: a seeded stream of requests (prompts uniform[64,1024],
 def serve_line(args):
     """Iteration-level batching driven through the kernels: the paged pool
     (admit by free blocks, grow block by block) against 4096-token
-    reservations on the same pool.  Each policy runs W untimed iterations
-    (the ramp-up), then K timed ones."""
-    from paged_kv_cache_400_amd.scheduler import Executor, Scheduler, seeded_requests
+    reservations on the same pool, decided by the C++ scheduler
+    (include/pa_scheduler.h).  Each policy runs W untimed iterations (the
+    ramp-up), then K timed ones."""
+    from paged_kv_cache_400_amd.scheduler import Executor, NativeScheduler, seeded_requests
     nb, K = 4096, args.serve_iterations
     res = {}
     for mode in ("paged", "reserved"):
         reqs = seeded_requests(20000, seed=6, prompt=(64, 1024), gen=(16, 512), rate=8.0)
-        sched = Scheduler(mode, reqs, num_blocks=nb, block_size=16, max_batch=256,
-                          max_step_tokens=2048)
+        sched = NativeScheduler(mode, reqs, num_blocks=nb, block_size=16, max_batch=256,
+                                max_step_tokens=2048)
         ex = Executor(nb, 16, 32, 8, 128, seed=6)
         ex.run(sched, K)
         st = ex.run(sched, K, timed=True)
@@ -705,7 +706,8 @@ def serve_line(args):
         "value": p["tokens_per_kernel_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": K, "ms_per_step": p["kernel_ms_per_iteration"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": SERVE_WORKLOAD, "num_blocks": nb, "block_size": 16},
+        "config": {"workload": SERVE_WORKLOAD, "num_blocks": nb, "block_size": 16,
+                   "scheduler": "C++ (include/pa_scheduler.h)"},
         "paged": p, "reserved": r,
         "paged_over_reserved": {
             "decode_batch": round(p["mean_decode_batch"] / r["mean_decode_batch"], 3),

@@ -23,8 +23,8 @@ _DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 # tensors) hold OCP E4M3 codes
 _POOL_DT = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
 
-# (name, restype, argtypes) for every entry point of include/pa.h, include/pa_probe.h and
-# include/pa_block_manager.h
+# (name, restype, argtypes) for every entry point of include/pa.h, include/pa_probe.h,
+# include/pa_block_manager.h and include/pa_scheduler.h
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -65,6 +65,12 @@ SIGNATURES = {
     "pa_bm_free": (ctypes.c_int, [_vp, ctypes.c_int64]),
     "pa_bm_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "pa_bm_block_refs": (_i32, [_vp, _i32]),
+    "pa_sched_create": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32]),
+    "pa_sched_step": (ctypes.c_int, [_vp, _vp]),
+    "pa_sched_active": (ctypes.c_int64, [_vp]),
+    "pa_sched_request": (ctypes.c_int, [_vp, ctypes.c_int64, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (ctypes.c_int32, []),
@@ -549,3 +555,90 @@ class BlockManager:
 
     def block_refs(self, block) -> int:
         return int(_lib.pa_bm_block_refs(self._h, int(block)))
+
+
+class _SchedPlan(ctypes.Structure):
+    """pa_sched_plan of include/pa_scheduler.h."""
+    _p64 = ctypes.POINTER(ctypes.c_int64)
+    _fields_ = [("iteration", ctypes.c_int64),
+                ("n_prefill", ctypes.c_int32), ("prefill", _p64),
+                ("n_decode", ctypes.c_int32), ("decode", _p64),
+                ("n_padded", ctypes.c_int32), ("padded", _p64),
+                ("n_admitted", ctypes.c_int32), ("admitted", _p64),
+                ("n_finished", ctypes.c_int32), ("finished", _p64),
+                ("n_preempted", ctypes.c_int32), ("preempted", _p64),
+                ("n_released", ctypes.c_int32), ("released", _p64),
+                ("running", ctypes.c_int32), ("queued", ctypes.c_int32),
+                ("blocks_used", ctypes.c_int64)]
+
+
+SCHED_MODES = {"static": 0, "reserved": 1, "paged": 2}
+
+
+class NativeSchedulerHandle:
+    """The C scheduler of include/pa_scheduler.h: create, add requests, step.
+    step() returns the plan as Python lists (copies; the C arrays are valid
+    only until the next step)."""
+
+    def __init__(self, mode, num_blocks, block_size, max_batch, max_step_tokens,
+                 reserve_tokens):
+        if mode not in SCHED_MODES:
+            raise ValueError(f"unknown mode {mode!r}")
+        h = ctypes.c_void_p()
+        _check(_lib.pa_sched_create(SCHED_MODES[mode], int(num_blocks), int(block_size),
+                                    int(max_batch), int(max_step_tokens), int(reserve_tokens),
+                                    ctypes.byref(h)))
+        self._h = h
+        self._plan = _SchedPlan()
+
+    def close(self):
+        if self._h:
+            _lib.pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, rids, arrivals, prompt_lens, gen_lens):
+        import numpy as np
+        r = np.ascontiguousarray(rids, dtype=np.int64)
+        a = np.ascontiguousarray(arrivals, dtype=np.int64)
+        p = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+        g = np.ascontiguousarray(gen_lens, dtype=np.int32)
+        if not (len(r) == len(a) == len(p) == len(g)):
+            raise ValueError("one arrival, prompt length and generation length per request")
+        _check(_lib.pa_sched_add(self._h, r.ctypes.data, a.ctypes.data, p.ctypes.data,
+                                 g.ctypes.data, len(r)))
+
+    def step(self):
+        """(iteration, dict of the plan's lists and counts)."""
+        pl = self._plan
+        st = _lib.pa_sched_step(self._h, ctypes.byref(pl))
+        if st != 0:
+            raise ValueError("a request is longer than a reservation"
+                             if st == 2 else f"pa_sched_step: status {st}")
+        def take(n, ptr):
+            return ptr[:n] if n else []
+        flat = take(3 * pl.n_prefill, pl.prefill)
+        return pl.iteration, {
+            "prefill": [tuple(flat[i:i + 3]) for i in range(0, len(flat), 3)],
+            "decode": take(pl.n_decode, pl.decode),
+            "padded": take(pl.n_padded, pl.padded),
+            "admitted": take(pl.n_admitted, pl.admitted),
+            "finished": take(pl.n_finished, pl.finished),
+            "preempted": take(pl.n_preempted, pl.preempted),
+            "released": take(pl.n_released, pl.released),
+            "running": pl.running, "queued": pl.queued, "blocks_used": pl.blocks_used}
+
+    def active(self) -> int:
+        return int(_lib.pa_sched_active(self._h))
+
+    def request(self, rid):
+        """(admitted, prefilled, generated, finished, released, preemptions);
+        -1 for an iteration that has not happened."""
+        out = (ctypes.c_int64 * 6)()
+        _check(_lib.pa_sched_request(self._h, int(rid), out))
+        return tuple(out)

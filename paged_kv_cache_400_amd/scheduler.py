@@ -82,6 +82,7 @@ class StepPlan:
     admitted: List[int] = field(default_factory=list)
     finished: List[int] = field(default_factory=list)
     preempted: List[int] = field(default_factory=list)
+    released: List[int] = field(default_factory=list)     # left the running set at the end
 
 
 class Scheduler:
@@ -101,6 +102,7 @@ class Scheduler:
         self.reserve_tokens = int(reserve_tokens)
         self.slots = self.num_blocks * self.bs // self.reserve_tokens  # reservations that fit
         self.pending = deque(sorted(requests, key=lambda r: (r.arrival, r.rid)))
+        self._prompt_len = {r.rid: r.prompt_len for r in self.pending}
         self.queue: deque = deque()
         self.running: List[Request] = []       # admission order
         self.done: List[Request] = []
@@ -109,6 +111,13 @@ class Scheduler:
 
     def blocks(self, tokens: int) -> int:
         return -(-tokens // self.bs)
+
+    def active(self) -> int:
+        """Requests pending, queued or running."""
+        return len(self.pending) + len(self.queue) + len(self.running)
+
+    def prompt_len_of(self, rid: int) -> int:
+        return self._prompt_len[rid]
 
     def blocks_used(self) -> int:
         """Paged: blocks the running requests hold now (Request.kv_tokens
@@ -148,11 +157,11 @@ class Scheduler:
                 r.finished = self.it
                 plan.finished.append(r.rid)
                 if self.mode != "static":
-                    self._release(r)
+                    self._release(r, plan)
         if self.mode == "static" and self.running and all(
                 r.finished is not None for r in self.running):
             for r in list(self.running):
-                self._release(r)
+                self._release(r, plan)
         self.history.append({"iteration": self.it, "running": len(self.running),
                              "decode": len(plan.decode), "padded": len(plan.padded),
                              "prefill_tokens": sum(k for _, _, k in plan.prefill),
@@ -222,10 +231,11 @@ class Scheduler:
         if r.rid in plan.admitted:
             plan.admitted.remove(r.rid)
 
-    def _release(self, r: Request):
+    def _release(self, r: Request, plan: StepPlan):
         self.running.remove(r)
         r.released = self.it
         self.done.append(r)
+        plan.released.append(r.rid)
 
     def run(self, max_iterations: int = 1_000_000) -> List[Request]:
         while (self.pending or self.queue or self.running) and self.it < max_iterations:
@@ -239,7 +249,77 @@ class Scheduler:
                 "mean_decode_batch": float(np.mean(dec)) if dec else 0.0,
                 "padded_rows": int(sum(x["padded"] for x in self.history)),
                 "max_running": max((x["running"] for x in self.history), default=0),
-                "preemptions": int(sum(r.preemptions for r in self.done + self.running))}
+                "preemptions": int(sum(r.preemptions
+                                       for r in self.done + self.running + list(self.queue)))}
+
+
+class NativeScheduler:
+    """The same scheduler in C++ (include/pa_scheduler.h, csrc/scheduler.cpp):
+    the same decisions as Scheduler, plan by plan (the tests compare them),
+    at a fraction of the host time per iteration.  Same constructor, step(),
+    active(), prompt_len_of(), history and summary() as Scheduler; `done`
+    holds the released requests' ids."""
+
+    def __init__(self, mode: str, requests, num_blocks: int, block_size: int = 16,
+                 max_batch: int = 256, max_step_tokens: int = 2048,
+                 reserve_tokens: int = 4096):
+        from .binding import NativeSchedulerHandle
+        self.mode = mode
+        self.bs = int(block_size)
+        self.num_blocks = int(num_blocks)
+        self.max_batch = int(max_batch)
+        self.reserve_tokens = int(reserve_tokens)
+        self.slots = self.num_blocks * self.bs // self.reserve_tokens
+        self._h = NativeSchedulerHandle(mode, num_blocks, block_size, max_batch,
+                                        max_step_tokens, reserve_tokens)
+        reqs = list(requests)
+        self._prompt_len = {r.rid: r.prompt_len for r in reqs}
+        self._rids = [r.rid for r in reqs]
+        if reqs:
+            self._h.add([r.rid for r in reqs], [r.arrival for r in reqs],
+                        [r.prompt_len for r in reqs], [r.gen_len for r in reqs])
+        self.it = 0
+        self.done: List[int] = []
+        self.history: List[Dict] = []
+
+    def step(self) -> StepPlan:
+        it, p = self._h.step()
+        self.it = it
+        plan = StepPlan(it, prefill=p["prefill"], decode=p["decode"], padded=p["padded"],
+                        admitted=p["admitted"], finished=p["finished"],
+                        preempted=p["preempted"], released=p["released"])
+        self.done.extend(plan.released)
+        self.history.append({"iteration": it, "running": p["running"],
+                             "decode": len(plan.decode), "padded": len(plan.padded),
+                             "prefill_tokens": sum(k for _, _, k in plan.prefill),
+                             "blocks_used": p["blocks_used"], "queued": p["queued"]})
+        return plan
+
+    def active(self) -> int:
+        return self._h.active()
+
+    def prompt_len_of(self, rid: int) -> int:
+        return self._prompt_len[rid]
+
+    def request(self, rid: int):
+        """(admitted, prefilled, generated, finished, released, preemptions)
+        of request rid, None for an iteration that has not happened."""
+        return tuple(None if (i in (0, 3, 4) and v < 0) else v
+                     for i, v in enumerate(self._h.request(rid)))
+
+    def run(self, max_iterations: int = 1_000_000) -> List[int]:
+        while self.active() and self.it < max_iterations:
+            self.step()
+        return self.done
+
+    def summary(self) -> Dict:
+        dec = [x["decode"] for x in self.history]
+        return {"mode": self.mode, "iterations": self.it, "finished": len(self.done),
+                "generated_tokens": int(sum(dec)),
+                "mean_decode_batch": float(np.mean(dec)) if dec else 0.0,
+                "padded_rows": int(sum(x["padded"] for x in self.history)),
+                "max_running": max((x["running"] for x in self.history), default=0),
+                "preemptions": int(sum(self._h.request(r)[5] for r in self._rids))}
 
 
 def seeded_requests(n: int, seed: int, prompt=(64, 1024), gen=(16, 512), rate: float = 4.0):
@@ -348,7 +428,6 @@ class Executor:
         """One scheduler step and the kernels it calls; returns the plan."""
         torch = self.torch
         plan = sched.step()
-        by_id = {r.rid: r for r in sched.running + sched.done}
         info = {}
         for rid in plan.preempted:
             if rid in self.kv_len:
@@ -379,7 +458,7 @@ class Executor:
             info["prefill"] = (prids, q, qs, bt_h, lens_h, out)
         # newest tokens of the running requests: append, then attend
         completes = {rid for rid, first, k in plan.prefill
-                     if first + k == by_id[rid].prompt_len}
+                     if first + k == sched.prompt_len_of(rid)}
         drids = [rid for rid in plan.decode if rid not in completes]
         if drids:
             rid_a = np.asarray(drids, np.int64)
@@ -402,9 +481,8 @@ class Executor:
                               scale=self.scale, workspace=self.ws)
             info["decode"] = (rows, q, bt_h, lens_h, out)
         # slots freed at the end of the iteration
-        for r in list(self.kv_len):
-            req = by_id.get(r)
-            if req is not None and req.released == sched.it:
+        for r in plan.released:
+            if r in self.kv_len:
                 self.bm.free(r)
                 del self.kv_len[r]
         if observe is not None:
@@ -423,7 +501,7 @@ class Executor:
         t0 = time.perf_counter()
         gen = dec_rows = pre = 0
         n = 0
-        while n < iterations and (sched.pending or sched.queue or sched.running):
+        while n < iterations and sched.active():
             plan = self.iteration(sched, observe)
             gen += len(plan.decode)
             dec_rows += len(plan.decode) + len(plan.padded)

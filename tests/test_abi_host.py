@@ -15,7 +15,8 @@ from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "pa.h")
 HEADERS = [HEADER, os.path.join(ROOT, "include", "pa_probe.h"),
-           os.path.join(ROOT, "include", "pa_block_manager.h")]
+           os.path.join(ROOT, "include", "pa_block_manager.h"),
+           os.path.join(ROOT, "include", "pa_scheduler.h")]
 LIB = os.path.join(ROOT, "paged_kv_cache_400_amd", "libpa.so")
 
 

@@ -15,21 +15,23 @@ import torch
 
 import oracle
 from _gpu import compare
-from paged_kv_cache_400_amd.scheduler import Executor, Scheduler, seeded_requests
+from paged_kv_cache_400_amd.scheduler import (Executor, NativeScheduler, Scheduler,
+                                              seeded_requests)
 from paged_kv_cache_400_amd.workload import bits
 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("cls", [Scheduler, NativeScheduler], ids=["python", "native"])
 @pytest.mark.parametrize("mode", ["paged", "reserved", "static"])
-def test_scheduler_drives_prefill_and_decode(mode):
+def test_scheduler_drives_prefill_and_decode(mode, cls):
     nb, bs = 48, 16
     reqs = seeded_requests(14, seed=5, prompt=(20, 200), gen=(3, 40), rate=1.5)
     kw = dict(block_size=bs, max_batch=8, max_step_tokens=64)
     if mode == "paged":
-        sched = Scheduler("paged", reqs, num_blocks=nb, **kw)
+        sched = cls("paged", reqs, num_blocks=nb, **kw)
     else:   # reservations of 256 tokens: 3 fit the pool
-        sched = Scheduler(mode, reqs, num_blocks=nb, reserve_tokens=256, **kw)
+        sched = cls(mode, reqs, num_blocks=nb, reserve_tokens=256, **kw)
     ex = Executor(nb, bs, num_q_heads=8, num_kv_heads=2, head_dim=64, seed=7)
     kt, vt = bits(ex.kv_table[:, 0].contiguous()), bits(ex.kv_table[:, 1].contiguous())
     counts = dict(prefill=0, decode=0, preempted=0)
