@@ -364,7 +364,8 @@ class Executor:
         self.rows = table_rows
         self.kv_table = torch.randn((table_rows, 2, self.hkv, self.d), generator=g).to(td)
         self.q_table = torch.randn((table_rows, self.hq, self.d), generator=g).to(td)
-        self.kv_dev = self.kv_table.to(self.device)
+        self.k_dev = self.kv_table[:, 0].contiguous().to(self.device)
+        self.v_dev = self.kv_table[:, 1].contiguous().to(self.device)
         self.q_dev = self.q_table.to(self.device)
         self.scale = float(np.float32(head_dim ** -0.5))
         self.kv_len: Dict[int, int] = {}      # tokens of each live request in the pool
@@ -399,30 +400,38 @@ class Executor:
         return ((np.asarray(rid, dtype=np.int64) << 16) ^
                 np.asarray(pos, dtype=np.int64)) & 0x3FFFFFFF
 
-    def _upload(self, a):
-        """A host array on the device without waiting for the GPU: staged in
-        pinned memory from torch's caching host allocator (which keeps the
-        staging buffer until the copy has run) and copied asynchronously on
-        the current stream, so the host can plan the next iteration while
-        the kernels run."""
-        t = self.torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
-        return t.to(self.device, non_blocking=True)
+    def _upload(self, *arrays):
+        """Host integer arrays (int32 values) on the device without waiting
+        for the GPU: packed into one pinned staging buffer from torch's
+        caching host allocator (which keeps it until the copy has run) and
+        copied asynchronously on the current stream, so the host can plan
+        the next iteration while the kernels run.  Returns int32 device views
+        of the arrays' shapes."""
+        torch = self.torch
+        sizes = [int(np.size(a)) for a in arrays]
+        buf = torch.empty(sum(sizes), dtype=torch.int32, pin_memory=True)
+        host = buf.numpy()
+        o = 0
+        for a, n in zip(arrays, sizes):
+            host[o:o + n] = np.asarray(a).reshape(-1)
+            o += n
+        dev = buf.to(self.device, non_blocking=True)
+        out, o = [], 0
+        for a, n in zip(arrays, sizes):
+            out.append(dev[o:o + n].view(np.shape(a)))
+            o += n
+        return out
 
     def _write(self, rows, slots):
-        """Append the key and value rows `rows` of the table at `slots`."""
-        if len(rows) == 0:
-            return
-        ix = self._upload(np.asarray(rows, np.int64))
-        kv = self.kv_dev.index_select(0, ix)
-        sl = self._upload(np.asarray(slots, dtype=np.int32))
-        k, v = kv[:, 0].contiguous(), kv[:, 1].contiguous()
-        self._timed(self.pa.reshape_and_cache, k, v, self.k_cache, self.v_cache, sl)
-        return kv, sl
+        """Append the key and value rows `rows` (device int32) of the tables
+        at `slots` (device int32)."""
+        k = self.k_dev.index_select(0, rows)
+        v = self.v_dev.index_select(0, rows)
+        self._timed(self.pa.reshape_and_cache, k, v, self.k_cache, self.v_cache, slots)
 
     def _tables(self, rids):
         mb = max(1, -(-max(self.kv_len[r] for r in rids) // self.bs))
-        t, lens = self.bm.tables(rids, mb)
-        return self._upload(t), self._upload(lens), t, lens
+        return self.bm.tables(rids, mb)
 
     def iteration(self, sched: Scheduler, observe=None):
         """One scheduler step and the kernels it calls; returns the plan."""
@@ -449,10 +458,11 @@ class Executor:
                 qs.append(qs[-1] + k)
                 prids.append(rid)
             rows = np.concatenate(q_rows)  # a token's q, key and value share its row
-            kv, sl = self._write(rows, np.concatenate(slots))
-            q = self.q_dev.index_select(0, self._upload(rows))
-            bt, lens, bt_h, lens_h = self._tables(prids)
-            qs_d = self._upload(np.asarray(qs, np.int32))
+            bt_h, lens_h = self._tables(prids)
+            rows_d, sl, bt, lens, qs_d = self._upload(rows, np.concatenate(slots), bt_h, lens_h,
+                                                      np.asarray(qs))
+            self._write(rows_d, sl)
+            q = self.q_dev.index_select(0, rows_d)
             out = self._timed(self.pa.prefill, q, self.k_cache, self.v_cache, bt, lens, qs_d,
                               scale=self.scale)
             info["prefill"] = (prids, q, qs, bt_h, lens_h, out)
@@ -460,6 +470,7 @@ class Executor:
         completes = {rid for rid, first, k in plan.prefill
                      if first + k == sched.prompt_len_of(rid)}
         drids = [rid for rid in plan.decode if rid not in completes]
+        new = []
         if drids:
             rid_a = np.asarray(drids, np.int64)
             pos = np.fromiter((self.kv_len[r] for r in drids), np.int64, len(drids))
@@ -467,12 +478,16 @@ class Executor:
             assert len(cow) == 0
             for r in drids:
                 self.kv_len[r] += 1
-            self._write(self.row_of(rid_a, pos), sl)
+            new = [self.row_of(rid_a, pos), sl]
         rows = drids + [rid for rid in plan.padded if rid in self.kv_len]
         if rows:
             last = np.fromiter((self.kv_len[r] - 1 for r in rows), np.int64, len(rows))
-            q = self.q_dev.index_select(0, self._upload(self.row_of(rows, last)))
-            bt, lens, bt_h, lens_h = self._tables(rows)
+            bt_h, lens_h = self._tables(rows)
+            up = self._upload(self.row_of(rows, last), bt_h, lens_h, *new)
+            if drids:
+                self._write(up[3], up[4])
+            q = self.q_dev.index_select(0, up[0])
+            bt, lens = up[1], up[2]
             need = self.pa.decode_workspace_bytes(len(rows), self.hq, self.d, bt.shape[1], self.bs)
             if self.ws is None or self.ws.numel() < need:
                 self.ws = torch.empty(max(need, 1 << 20) * 2, dtype=torch.uint8,
