@@ -515,12 +515,6 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
                   const int32_t* __restrict__ seq_lens, int32_t num_pairs, int32_t hkv,
                   int32_t max_len) {
   static_assert(TPP == 64 || TPP == 256, "a wave or a workgroup per pair");
-  // partials read per round trip.  With few pairs (a workgroup each) a pair
-  // may be cut into many runs -- 61 partials per pair of a long sequence on
-  // the pages' worked example, merged 16 at a time in 6.7 us against 10.3 us
-  // 4 at a time.  Many pairs (a wave each) have one or two partials, and
-  // 16 loads per round, mostly predicated off, cost 4,096 short sequences 3%.
-  constexpr int kBatch = TPP == 256 ? 16 : 4;
   const int lane = threadIdx.x % TPP;
   const int pair = blockIdx.x * (256 / TPP) + threadIdx.x / TPP;
   if (pair >= num_pairs) return;
@@ -536,47 +530,60 @@ pa_streamk_reduce(uint16_t* __restrict__ out, const float* __restrict__ ws_acc,
   }
   const int c_first = meta.x, c_last = meta.y;
   if (c_first == c_last) return;  // finished by one wave
-  for (int i = lane * 4; i < G * D; i += TPP * 4) {
-    const int h = i / D, d = i % D;
-    float M = kNegInf, den = 0.0f;
-    float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c0 = c_first; c0 <= c_last; c0 += kBatch) {
-      float2 ml[kBatch];
-      float4 a[kBatch];
+  // the pair's partials, kBatch read per round trip
+  auto merge = [&](auto batch) {
+    constexpr int kBatch = decltype(batch)::value;
+    for (int i = lane * 4; i < G * D; i += TPP * 4) {
+      const int h = i / D, d = i % D;
+      float M = kNegInf, den = 0.0f;
+      float num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int c0 = c_first; c0 <= c_last; c0 += kBatch) {
+        float2 ml[kBatch];
+        float4 a[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int c = c0 + u;
-        ml[u] = make_float2(kNegInf, 0.0f);
-        a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (c <= c_last) {
-          const int64_t slot = 2 * ((int64_t)c * hkv + kh) + (c == c_first ? meta.z : 0);
-          ml[u] = ws_ml[slot * G + h];
-          a[u] = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
+        for (int u = 0; u < kBatch; ++u) {
+          const int c = c0 + u;
+          ml[u] = make_float2(kNegInf, 0.0f);
+          a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (c <= c_last) {
+            const int64_t slot = 2 * ((int64_t)c * hkv + kh) + (c == c_first ? meta.z : 0);
+            ml[u] = ws_ml[slot * G + h];
+            a[u] = *reinterpret_cast<const float4*>(ws_acc + (slot * G + h) * D + d);
+          }
         }
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
+        const float base = (Mb == kNegInf) ? 0.0f : Mb;
+        const float r = exp2_fast(M - base);  // rescale what is summed so far
+        den *= r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] *= r;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float f = exp2_fast(ml[u].x - base);
+          den = fmaf(f, ml[u].y, den);
+          num[0] = fmaf(f, a[u].x, num[0]);
+          num[1] = fmaf(f, a[u].y, num[1]);
+          num[2] = fmaf(f, a[u].z, num[2]);
+          num[3] = fmaf(f, a[u].w, num[3]);
+        }
+        M = Mb;
       }
-      float Mb = M;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
-      const float base = (Mb == kNegInf) ? 0.0f : Mb;
-      const float r = exp2_fast(M - base);  // rescale what is summed so far
-      den *= r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] *= r;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float f = exp2_fast(ml[u].x - base);
-        den = fmaf(f, ml[u].y, den);
-        num[0] = fmaf(f, a[u].x, num[0]);
-        num[1] = fmaf(f, a[u].y, num[1]);
-        num[2] = fmaf(f, a[u].z, num[2]);
-        num[3] = fmaf(f, a[u].w, num[3]);
-      }
-      M = Mb;
+      const uint2 o = make_uint2(pack2<T>(num[0] / den, num[1] / den),
+                                 pack2<T>(num[2] / den, num[3] / den));
+      *reinterpret_cast<uint2*>(out + (row0 + h) * D + d) = o;
     }
-    const uint2 o = make_uint2(pack2<T>(num[0] / den, num[1] / den),
-                               pack2<T>(num[2] / den, num[3] / den));
-    *reinterpret_cast<uint2*>(out + (row0 + h) * D + d) = o;
-  }
+  };
+  // A pair cut into many runs (a long sequence in a small batch: 61 partials
+  // per pair of the pages' worked example) is merged 16 partials per round
+  // trip (6.6 us against 10.3 us 4 at a time); the usual one or two
+  // partials 4 at a time (16, mostly predicated off, cost the mixed step
+  // 0.5 us and 4,096 short sequences 3%).
+  if (TPP == 256 && c_last - c_first >= 4)
+    merge(std::integral_constant<int, 16>{});
+  else
+    merge(std::integral_constant<int, 4>{});
 }
 
 // The merge of pa_decode_shared_prefix, one workgroup per (sequence, KV
