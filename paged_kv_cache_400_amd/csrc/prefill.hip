@@ -165,6 +165,11 @@ __device__ __forceinline__ void read_v_slab(uint2 (&lo)[NM], uint2 (&hi)[NM],
   }
 }
 
+// The larger of a and b, NaN if either is NaN (llvm.maximum).
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Two 16-bit ones packed in a word (the B operand of a row sum).
 template <typename T> constexpr uint32_t kOnes2 = 0x3c003c00u;  // fp16 1.0
 template <> constexpr uint32_t kOnes2<BF16> = 0x3f803f80u;      // bf16 1.0
@@ -496,6 +501,11 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         k1[c] = *reinterpret_cast<const uint4*>(kb + (KC + c) * SG::KBLK);
       }
       uint4 pa_op[kNrb];
+      // only slabs that reach past the first token's end need the mask (an
+      // int in a scalar register: as a bool kept across the row blocks'
+      // code the compiler carried it in a vector register, two
+      // instructions per use)
+      const int masked = __builtin_amdgcn_readfirstlane((int)(t0 + 2 * kTile > wave_min_end));
 #pragma unroll
       for (int h = 0; h < kNrb; ++h) {
         f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -503,18 +513,20 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int c = 0; c < KC; ++c) s0 = mfma_k32<T>(k0[c], qb[h][c], s0);
 #pragma unroll
         for (int c = 0; c < KC; ++c) s1 = mfma_k32<T>(k1[c], qb[h][c], s1);
-        // only slabs that reach past the first token's end need the mask;
         // rows of tokens past the chunk are never stored
-        if (t0 + 2 * kTile > wave_min_end) {
+        if (masked) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (t0 + 4 * grp + r >= lane_end[h]) s0[r] = kNegInf;
             if (t0 + kTile + 4 * grp + r >= lane_end[h]) s1[r] = kNegInf;
           }
         }
-        const float lm =
-            fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                  fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * sc_scale;
+        // the lane's largest score: llvm.maximum maps to v_maximum3_f32,
+        // four instructions for the eight scores; fmaxf's IEEE semantics had
+        // the compiler quiet each raw matrix-core result first (eleven)
+        const float ma = fmax_nan(fmax_nan(s0[0], s0[1]), s0[2]);
+        const float mb = fmax_nan(fmax_nan(s0[3], s1[0]), s1[1]);
+        const float lm = fmax_nan(mb, fmax_nan(fmax_nan(s1[2], s1[3]), ma)) * sc_scale;
         if (__builtin_amdgcn_ballot_w64(lm > m_run[h] + kRescaleSlack) != 0) {
           float mx = fmaxf(lm, __shfl_xor(lm, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
