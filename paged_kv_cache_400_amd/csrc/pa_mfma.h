@@ -140,6 +140,55 @@ __device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
   return v;
 }
 
+// read_v_tr, each read issued twice, into w and w2: an operand that holds
+// the same 64 bits twice (the V operand of the hi and lo weights) then comes
+// straight from the reads, where a copy of one read took two moves per
+// matrix-core product.  The second reads hit the same LDS lines.
+template <int NM>
+__device__ __forceinline__ void read_v_tr_twice(uint2 (&w)[NM], uint2 (&w2)[NM], uint32_t a) {
+  static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
+  if constexpr (NM == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %8, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:32\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:96\n\t"
+        "ds_read_b64_tr_b16 %11, %16 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:160\n\t"
+        "ds_read_b64_tr_b16 %13, %16 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %16 offset:224\n\t"
+        "ds_read_b64_tr_b16 %15, %16 offset:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
+          "=&v"(w[6]), "=&v"(w[7]), "=&v"(w2[0]), "=&v"(w2[1]), "=&v"(w2[2]), "=&v"(w2[3]),
+          "=&v"(w2[4]), "=&v"(w2[5]), "=&v"(w2[6]), "=&v"(w2[7])
+        : "v"(a)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %4, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w2[0]), "=&v"(w2[1]),
+          "=&v"(w2[2]), "=&v"(w2[3])
+        : "v"(a)
+        : "memory");
+  }
+}
+
 // The NM transpose reads of a V tile for one lane (column block m at byte
 // offset 32 m from the lane's LDS address a), as one asm block that waits for
 // its own results before it ends.  Written as builtins, these reads would
@@ -263,7 +312,7 @@ struct TileWave {
     {
       const int t = min(t0 + col, t_last);
       const uint16_t* kr_base = (BS < kTile && t - t0 >= BS) ? kb1 : kb0;
-      const uint16_t* ptr = kr_base + (t % BS) * D + grp * 8;
+      const uint16_t* ptr = kr_base + ((uint32_t)t % BS) * D + grp * 8;
 #pragma unroll
       for (int c = 0; c < KC; ++c) kr[c] = load_stream(ptr + c * 32);
     }
@@ -274,7 +323,8 @@ struct TileWave {
     for (int i = 0; i < 4; ++i) {
       const int tau = 4 * i + lane / (D / 8);
       const int t = min(t0 + tau, t_last);
-      const uint16_t* vrow = ((BS < kTile && t - t0 >= BS) ? vb1 : vb0) + (t % BS) * D;
+      const uint16_t* vrow =
+          ((BS < kTile && t - t0 >= BS) ? vb1 : vb0) + ((uint32_t)t % BS) * D;
       if (GE::LANES == 64 || lane < GE::LANES)
         __builtin_amdgcn_global_load_lds(
             (const void*)(vrow + (lane % (D / 8)) * 8),
@@ -297,7 +347,9 @@ struct TileWave {
   // the second one unless all of them clamp back into the first).
   // kNt: the streaming hint on every load (each byte read once, the batch's
   // K/V far larger than the caches); without it, K/V that the last-level
-  // cache holds is read from there.
+  // cache holds is read from there.  Positions are never negative: the row
+  // within a block is an unsigned remainder, one AND (signed, five
+  // instructions per address).
   static constexpr int kLoadsPerTile = KL + 4;
   template <bool kNt = true>
   __device__ __forceinline__ void issue_ids_counted(uint4 (&kr)[KC], int buf, int t0, int t_last,
@@ -307,7 +359,8 @@ struct TileWave {
       const uint16_t* kb0 = kc + (int64_t)id0 * blk_stride + head_off;
       const uint16_t* kb1 = kc + (int64_t)id1 * blk_stride + head_off;
       const int t = min(t0 + col, t_last);
-      const uint16_t* ptr = ((BS < kTile && t - t0 >= BS) ? kb1 : kb0) + (t % BS) * D + grp * 8;
+      const uint16_t* ptr =
+          ((BS < kTile && t - t0 >= BS) ? kb1 : kb0) + ((uint32_t)t % BS) * D + grp * 8;
 #pragma unroll
       for (int c = 0; c < KC; ++c) kr[c] = load_kv<kNt>(ptr + c * 32);
     }
@@ -320,7 +373,7 @@ struct TileWave {
     for (int i = 0; i < 4; ++i) {
       const int t = min(t0 + 4 * i + lane / (D / 8), t_last);
       const bool second = BS < kTile && 4 * i >= BS && t0 + BS <= t_last;
-      const uint32_t off = (uint32_t)(((t % BS) * D + (lane % (D / 8)) * 8) * 2);
+      const uint32_t off = (((uint32_t)t % BS) * D + (lane % (D / 8)) * 8) * 2;
       if (GE::LANES == 64 || lane < GE::LANES)
         copy_to_lds16<kNt ? kCachePolicyStream : kCachePolicyReuse>(second ? r1 : r0, off,
                                                                      vt + i * GE::REGION);
@@ -356,14 +409,14 @@ struct TileWave {
       const float corr = exp2_fast(m_run - m_new);  // 0 when m_run = -inf
       m_run = m_new;
       l_run *= corr;
-      float cr[4];
+      // as whole vectors: scaled element by element, the accumulators
+      // took new registers, and the path without a rescale copied them
+      // there (16 moves a tile)
+      f32x4_t cr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
-      }
+      for (int m = 0; m < NM; ++m) acc[m] = acc[m] * cr;
     }
     float pw[4];
 #pragma unroll
@@ -378,12 +431,12 @@ struct TileWave {
     // row.
     const unsigned char* vb = vtile + buf * GE::TILE + grp * GE::REGION + (col >> 2) * GE::ROW +
                               8 * (col & 3);
-    uint2 w[NM];
+    uint2 w[NM], w2[NM];
     if constexpr (kDrain) wait_vmem_all();
-    read_v_tr<NM>(w, (uint32_t)(uintptr_t)vb);
+    read_v_tr_twice<NM>(w, w2, (uint32_t)(uintptr_t)vb);
 #pragma unroll
     for (int m = 0; m < NM; ++m)
-      acc[m] = mfma_k32<T>(pa_op, make_uint4(w[m].x, w[m].y, w[m].x, w[m].y), acc[m]);
+      acc[m] = mfma_k32<T>(pa_op, make_uint4(w[m].x, w[m].y, w2[m].x, w2[m].y), acc[m]);
   }
 
   // After the last tile: every lane holds head col's whole denominator.

@@ -172,25 +172,32 @@ struct TileWave8 {
     l_run = 0.0f;
   }
 
-  // Block of position t (t0 <= t < t0 + 32) from the tile's ids.
-  __device__ __forceinline__ int block_of(int t, int t0, const int (&ids)[kIds]) const {
-    int id = ids[0];
+  // Byte offset of the KV head's rows in the block holding position t
+  // (t0 <= t < t0 + 32), picked from the tile's block offsets.
+  __device__ __forceinline__ uint64_t block_of(int t, int t0, const uint64_t (&boff)[kIds]) const {
+    uint64_t o = boff[0];
 #pragma unroll
     for (int j = 1; j < kIds; ++j)
-      if (t - t0 >= j * BS) id = ids[j];
-    return id;
+      if (t - t0 >= j * BS) o = boff[j];
+    return o;
   }
 
   // Issue the K (registers) and V (LDS buffer buf) loads of the tile at
   // positions t0..t0+31, clamped to t_last; ids[j] is the block of positions
-  // t0 + j * BS ... (entries past t_last are not used).
+  // t0 + j * BS ... (entries past t_last are not used).  The ids are the
+  // same in every lane, so their offsets are scalar work; a lane only
+  // picks one.  Positions are never negative: the row within a block is an
+  // unsigned remainder, one AND (signed, five instructions).
   __device__ __forceinline__ void issue_ids(uint4 (&kr)[KL], int buf, int t0, int t_last,
                                             const int (&ids)[kIds]) {
+    uint64_t boff[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j)
+      boff[j] = (uint64_t)(uint32_t)ids[j] * (uint64_t)blk_stride + (uint64_t)head_off;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = min(t0 + 16 * u + col, t_last);
-      const uint8_t* p = kc + (int64_t)block_of(t, t0, ids) * blk_stride + head_off +
-                         (t % BS) * D + grp * 16;
+      const uint8_t* p = kc + block_of(t, t0, boff) + ((uint32_t)t % BS) * D + grp * 16;
 #pragma unroll
       for (int c = 0; c < KCH; ++c) kr[u * KCH + c] = load_stream(p + c * 64);
     }
@@ -202,8 +209,7 @@ struct TileWave8 {
     for (int i = 0; i < 4; ++i) {
       const int tau = r8 < 4 ? 4 * i + r8 : 16 + 4 * i + (r8 - 4);
       const int t = min(t0 + tau, t_last);
-      const uint8_t* vrow = vc + (int64_t)block_of(t, t0, ids) * blk_stride + head_off +
-                            (t % BS) * D;
+      const uint8_t* vrow = vc + block_of(t, t0, boff) + ((uint32_t)t % BS) * D;
       if (GE::LANES == 64 || lane < GE::LANES)
         __builtin_amdgcn_global_load_lds(
             (const void*)(vrow + (lane % (D / 16)) * 16),
@@ -244,14 +250,11 @@ struct TileWave8 {
       const float corr = exp2_fast(m_run - m_new);  // 0 when m_run = -inf
       m_run = m_new;
       l_run *= corr;
-      float cr[4];
+      f32x4_t cr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][r] *= cr[r];
-      }
+      for (int m = 0; m < NM; ++m) acc[m] = acc[m] * cr;
     }
     float pw[8];
 #pragma unroll

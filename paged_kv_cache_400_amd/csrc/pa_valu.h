@@ -90,25 +90,31 @@ struct TileWaveV {
     }
   }
 
-  // Block of position t (t0 <= t < t0 + 16) from the tile's ids.
-  __device__ __forceinline__ int block_of(int t, int t0, const int (&ids)[kIds]) const {
-    int id = ids[0];
+  // Offset (elements) of the KV head's rows in the block holding position
+  // t (t0 <= t < t0 + 16), picked from the tile's block offsets.
+  __device__ __forceinline__ uint64_t block_of(int t, int t0, const uint64_t (&boff)[kIds]) const {
+    uint64_t o = boff[0];
 #pragma unroll
     for (int j = 1; j < kIds; ++j)
-      if (t - t0 >= j * BS) id = ids[j];
-    return id;
+      if (t - t0 >= j * BS) o = boff[j];
+    return o;
   }
 
   // Issue the K and V loads of the tile at positions t0..t0+15, clamped to
   // t_last (a clamped row re-reads the last valid position; its score is
-  // masked).  ids[j] is the block of positions t0 + j * BS ...
+  // masked).  ids[j] is the block of positions t0 + j * BS ...; the ids are
+  // the same in every lane, so their offsets are scalar work.  Positions are
+  // never negative: the row within a block is an unsigned remainder.
   __device__ __forceinline__ void issue_ids(uint4 (&kr)[KL], int, int t0, int t_last,
                                             const int (&ids)[kIds]) {
+    uint64_t boff[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j)
+      boff[j] = (uint64_t)(uint32_t)ids[j] * (uint64_t)blk_stride + (uint64_t)head_off;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = min(t0 + i * RPL + row, t_last);
-      const int64_t off =
-          (int64_t)block_of(t, t0, ids) * blk_stride + head_off + (t % BS) * D + col * 8;
+      const uint64_t off = block_of(t, t0, boff) + ((uint32_t)t % BS) * D + col * 8;
       kr[i] = load_stream(kc + off);
       kr[NI + i] = load_stream(vc + off);
     }

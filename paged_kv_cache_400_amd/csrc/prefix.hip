@@ -201,7 +201,7 @@ pa_prefix_attend(float* __restrict__ pre_acc, float2* __restrict__ pre_ml,
       }
       const int id = __builtin_amdgcn_ds_bpermute(4 * (t / BS - blk_base), vid);
       const uint16_t* src = (jb < KC ? kc : vc) + (int64_t)id * blk_stride + head_off +
-                            (t % BS) * D + chunk8 * 8;
+                            ((uint32_t)t % BS) * D + chunk8 * 8;
       // the default cache policy: the (head, chunk)'s other workgroups copy
       // the same tile from this L2 (43.5-43.9 against 44.1-44.2 us per call
       // with the streaming hint)
