@@ -133,17 +133,24 @@ __device__ __forceinline__ void stage_mfma_result(float* st, const f32x4_t (&acc
 }
 
 // One 32-bit LDS read at byte address a, completed before the asm ends (for
-// the reason given at read_v_tr).
+// the reason given at read_v_tr_twice).
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
   return v;
 }
 
-// read_v_tr, each read issued twice, into w and w2: an operand that holds
-// the same 64 bits twice (the V operand of the hi and lo weights) then comes
-// straight from the reads, where a copy of one read took two moves per
-// matrix-core product.  The second reads hit the same LDS lines.
+// The NM transpose reads of a V tile for one lane (column block m at byte
+// offset 32 m from the lane's LDS address a), as one asm block that waits for
+// its own results before it ends.  Written as builtins, these reads would
+// make the compiler wait first for every LDS copy the wave has in flight (it
+// cannot tell the buffers apart), the next tiles' copies included; a driver
+// that keeps several tiles in flight must not lose them there.  The
+// caller's own vmcnt wait orders the reads after this tile's copies.
+// Each read is issued twice, into w and w2: an operand that holds the same
+// 64 bits twice (the V operand of the hi and lo weights) then comes straight
+// from the reads, where a copy of one read took two moves per matrix-core
+// product.  The second reads hit the same LDS lines.
 template <int NM>
 __device__ __forceinline__ void read_v_tr_twice(uint2 (&w)[NM], uint2 (&w2)[NM], uint32_t a) {
   static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
@@ -184,44 +191,6 @@ __device__ __forceinline__ void read_v_tr_twice(uint2 (&w)[NM], uint2 (&w2)[NM],
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w2[0]), "=&v"(w2[1]),
           "=&v"(w2[2]), "=&v"(w2[3])
-        : "v"(a)
-        : "memory");
-  }
-}
-
-// The NM transpose reads of a V tile for one lane (column block m at byte
-// offset 32 m from the lane's LDS address a), as one asm block that waits for
-// its own results before it ends.  Written as builtins, these reads would
-// make the compiler wait first for every LDS copy the wave has in flight (it
-// cannot tell the buffers apart), the next tiles' copies included; a driver
-// that keeps several tiles in flight must not lose them there.  The
-// caller's own vmcnt wait orders the reads after this tile's copies.
-template <int NM>
-__device__ __forceinline__ void read_v_tr(uint2 (&w)[NM], uint32_t a) {
-  static_assert(NM == 4 || NM == 8, "head_dim 64 or 128");
-  if constexpr (NM == 8) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:224\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
-          "=&v"(w[6]), "=&v"(w[7])
-        : "v"(a)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:32\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
-        "ds_read_b64_tr_b16 %3, %4 offset:96\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
         : "v"(a)
         : "memory");
   }

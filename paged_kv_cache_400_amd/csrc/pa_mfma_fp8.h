@@ -75,7 +75,7 @@ template <typename T> __device__ __forceinline__ uint4 widen8(uint32_t w0, uint3
 
 // The NM byte-transpose reads of an 8-bit V tile for one lane (column block
 // m at byte offset 16 m from a), as one asm block that waits for its own
-// results, for the reason given at read_v_tr: builtins would make the
+// results, for the reason given at read_v_tr_twice: builtins would make the
 // compiler wait for every LDS copy in flight, the next tiles' included.
 template <int NM>
 __device__ __forceinline__ void read_v_tr8(uint2 (&w)[NM], uint32_t a) {

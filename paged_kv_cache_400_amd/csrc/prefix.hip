@@ -85,7 +85,7 @@ __device__ __forceinline__ void wait_own_tiles(int w) {
 }
 
 // The KC 16-byte K operands of this lane from a K tile in LDS, read as one
-// asm block that waits for its own results (the reason is read_v_tr's).
+// asm block that waits for its own results (the reason is read_v_tr_twice's).
 template <int KC>
 __device__ __forceinline__ void read_k(uint4 (&kr)[KC], uint32_t a) {
   static_assert(KC == 2 || KC == 4, "head_dim 64 or 128");
