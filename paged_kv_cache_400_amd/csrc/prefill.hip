@@ -501,11 +501,6 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         k1[c] = *reinterpret_cast<const uint4*>(kb + (KC + c) * SG::KBLK);
       }
       uint4 pa_op[kNrb];
-      // only slabs that reach past the first token's end need the mask (an
-      // int in a scalar register: as a bool kept across the row blocks'
-      // code the compiler carried it in a vector register, two
-      // instructions per use)
-      const int masked = __builtin_amdgcn_readfirstlane((int)(t0 + 2 * kTile > wave_min_end));
 #pragma unroll
       for (int h = 0; h < kNrb; ++h) {
         f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -513,8 +508,9 @@ pa_prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int c = 0; c < KC; ++c) s0 = mfma_k32<T>(k0[c], qb[h][c], s0);
 #pragma unroll
         for (int c = 0; c < KC; ++c) s1 = mfma_k32<T>(k1[c], qb[h][c], s1);
+        // only slabs that reach past the first token's end need the mask;
         // rows of tokens past the chunk are never stored
-        if (masked) {
+        if (t0 + 2 * kTile > wave_min_end) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (t0 + 4 * grp + r >= lane_end[h]) s0[r] = kNegInf;
