@@ -44,6 +44,20 @@ def test_many_short_sequences(part):
     compare(out, oracle_out(b, kp, vp), label=f"many_short part{part}", round_slack=True)
 
 
+@pytest.mark.parametrize("L", [512, 513, 640, 641, 2048, 2049, 2176])
+def test_merge_of_four_to_seventeen_partials(L):
+    """One sequence alone: the balanced split cuts each (sequence, KV head)
+    pair into runs of 8 tiles of 16 positions, so L = 512 leaves 4 partials
+    per pair, 513 and 640 five, 641 six, 2048 sixteen, 2049 and 2176
+    seventeen.  The merge reads a pair's partials 4 per round trip up to 4
+    of them and 16 per round trip from 5 on (the last round trip partly
+    empty); every count must give the oracle's rows."""
+    b = wl.make_decode_batch(f"merge_{L}", [L], 32, 8, 128, 16, "bf16", seed=41 + L, append=0)
+    out, dev = gpu_step(b)
+    kp, vp = oracle_pools(b)
+    compare(out, oracle_out(b, kp, vp), label=f"merge L={L}", round_slack=True)
+
+
 @pytest.mark.parametrize("impl", ["auto", "mfma", "valu"])
 def test_runs_across_many_sequences_group8(impl):
     """Group 8 with each tile wave: short sequences (empty ones among them)
