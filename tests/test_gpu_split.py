@@ -44,6 +44,21 @@ def test_many_short_sequences(part):
     compare(out, oracle_out(b, kp, vp), label=f"many_short part{part}", round_slack=True)
 
 
+def test_runs_found_across_ten_batches_of_lengths():
+    """2,500 sequences (lengths read 256 at a time: ten batches), short ones
+    with a few long ones and empty ones among them: each wave finds its
+    run's first sequence from the start of the lengths and its last from the
+    batch where the first was found, so the runs' ends fall in every batch."""
+    rng = np.random.default_rng(51)
+    lens = rng.integers(0, 48, 2500).tolist()
+    for i, L in ((7, 1500), (900, 0), (1300, 3000), (2499, 700)):
+        lens[i] = L
+    b = wl.make_decode_batch("ten_batches", lens, 32, 8, 128, 16, "bf16", seed=52, append=1)
+    out, dev = gpu_step(b)
+    kp, vp = oracle_pools(b)
+    compare(out, oracle_out(b, kp, vp), label="ten batches", round_slack=True)
+
+
 @pytest.mark.parametrize("L", [512, 513, 640, 641, 2048, 2049, 2176])
 def test_merge_of_four_to_seventeen_partials(L):
     """One sequence alone: the balanced split cuts each (sequence, KV head)
