@@ -122,9 +122,11 @@ struct TileWaveOf<T, Vec, D, BS, G> {
 // FP8 with out_scale = v_scale applied to every result; for 16-bit pools
 // out_scale is not used).  Two waves per SIMD are all the launch uses
 // (kWorkgroupsPerCu), so the compiler may take up to 256 registers; at
-// d 128 the 8-bit tile wave uses 219 of them (with the 168 that three waves
-// allow it spent 8% more time on the mixed step), the vector-unit one up to
-// 222 and the 16-bit matrix-core one 175.
+// d 128 and block 16 the 8-bit tile wave uses 207-217 of them (with the 168
+// that three waves allow it spent 8% more time on the mixed step), the
+// 16-bit matrix-core one 183-195, the vector-unit one 148-256 (at group 8
+// all of them, and it spills 80-160 bytes per lane; the 8-bit one spills
+// 48 bytes at block 8).
 //
 // kDeep: each wave with two tiles in flight instead of one (the 16-bit
 // matrix-core tile wave only, whose loads the compiler counts exactly; see
